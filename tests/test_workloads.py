@@ -1,0 +1,63 @@
+"""CPU tests of the seeded input generator and FLOP accounting."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10.0,
+                        np.array([0.0, -0.0, 1.0, 1.00390625, 1.0078125, 3.4e38, -3.4e38,
+                                  1e-40, np.inf, -np.inf], dtype=np.float32)])
+    # halfway cases: bit 15 set with nothing below -> ties to even
+    u = rng.integers(0, 2**31, 1000, dtype=np.uint32) & 0x7F7F0000 | 0x8000
+    x = np.concatenate([x, u.view(np.float32)])
+    ours = W.round_to_bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(ours.view(np.uint32), ref.view(np.uint32))
+
+
+def test_f16_rounding_matches_torch():
+    x = np.random.default_rng(1).standard_normal(100000).astype(np.float32) * 100
+    ref = torch.from_numpy(x).to(torch.float16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(W.round_to_f16(x), ref)
+
+
+def test_inputs_are_deterministic_and_exact_in_dtype():
+    w = W.WORKLOADS["gqa_f16_4k"]
+    a = W.make_inputs(w, N=64)
+    b = W.make_inputs(w, N=64)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    q, k, v = a
+    assert q.shape == (4, 32, 64, 128) and k.shape == (4, 8, 64, 128)
+    np.testing.assert_array_equal(W.round_to_f16(q), q)
+    # the outlier channel: one K channel is 8x the others in scale
+    per_channel = np.abs(k).mean(axis=(0, 1, 2))
+    c = int(per_channel.argmax())
+    assert per_channel[c] > 5 * np.median(per_channel)
+    w3 = W.WORKLOADS["causal_8k"]
+    q3, _, _ = W.make_inputs(w3, B=1, Hq=1, Hkv=1, N=256)
+    assert 0.4 < q3.std() < 0.6          # N(0,1) * 0.5
+    np.testing.assert_array_equal(W.round_to_bf16(q3), q3)
+
+
+@pytest.mark.parametrize("N,causal,wl", [(1, False, -1), (7, True, -1), (7, False, 2), (9, True, 3),
+                                         (10, True, 0), (5, True, 100)])
+def test_unmasked_pairs_brute_force(N, causal, wl):
+    cnt = sum(1 for i in range(N) for j in range(N)
+              if not ((causal and j > i) or (wl >= 0 and j < i - wl)))
+    assert W.unmasked_pairs(N, causal, wl) == cnt
+
+
+def test_metric_flops_headline_values():
+    assert W.metric_flops(W.WORKLOADS["causal_8k"]) == 4 * 2 * 16 * 8192 ** 2 * 128 / 2
+    assert math.isclose(W.metric_flops(W.WORKLOADS["causal_8k"]), 5.4976e11, rel_tol=1e-4)
+    # sliding window: exact kept pairs; 125,859,840 per head at N=32768, wl=4096
+    assert W.unmasked_pairs(32768, True, 4096) == 125859840
+    assert math.isclose(W.metric_flops(W.WORKLOADS["swa_32k"]), 2.0621e12, rel_tol=1e-4)
+    assert W.metric_flops(W.WORKLOADS["bf16_n1k_d64"]) == 4 * 8 * 16 * 1024 ** 2 * 64

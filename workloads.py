@@ -1,0 +1,158 @@
+"""Seeded synthetic inputs for exact attention, shared by the tests, the bench
+and the smoke check.
+
+This module draws random numbers and rounds them to the storage type; it holds
+none of the attention arithmetic (no scores, no softmax, no products), so both
+the CPU oracle's callers and the GPU path's callers can use it without the two
+sharing any of the method's code.
+
+Workloads: the five shapes are the ones the attention forward is measured on.
+The pages fix no dataset (the FlashAttention-2 (PL) article quotes GPT-style
+training, section "Wydajność i efektywność"), so every input is i.i.d. normal
+noise of the stated shape, drawn from numpy's PCG64 with a fixed seed.
+
+Draw order, per workload: Q, then K, then V, each ``standard_normal`` in float32
+over the contiguous [B][H][N][d] shape; then the workload's transform (a scalar
+multiplier, or one K channel scaled by 8 with the channel index drawn next from
+the same generator); then round-to-nearest-even to the storage type.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+DTYPES = ("f32", "f16", "bf16")
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    causal: bool
+    window_left: int  # -1 = no window
+    seed: int
+    value_mult: float = 1.0       # multiplier applied to Q, K and V before rounding
+    k_outlier_mult: float = 0.0   # >0: one K channel (same for every row/head) times this
+
+    @property
+    def scale(self) -> float:
+        """softmax scale 1/sqrt(d), as the float32 value handed to the kernel."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five measured shapes.  "tiny" is small enough for the oracle to finish in
+# milliseconds; "causal_8k" is the headline (GPT-style training shape).
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", "f32", 1, 1, 1, 128, 64, False, -1, 0),
+    "bf16_n1k_d64": Workload("bf16_n1k_d64", "bf16", 8, 16, 16, 1024, 64, False, -1, 1),
+    "causal_8k": Workload("causal_8k", "bf16", 2, 16, 16, 8192, 128, True, -1, 2, value_mult=0.5),
+    "gqa_f16_4k": Workload("gqa_f16_4k", "f16", 4, 32, 8, 4096, 128, True, -1, 3, k_outlier_mult=8.0),
+    "swa_32k": Workload("swa_32k", "bf16", 1, 32, 32, 32768, 128, True, 4096, 4),
+}
+ORDER = ["tiny_f32", "bf16_n1k_d64", "causal_8k", "gqa_f16_4k", "swa_32k"]
+HEADLINE = "causal_8k"
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 to the nearest bfloat16 (ties to even); returned as float32.
+
+    NaN stays NaN (quiet); infinities stay infinite.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = (u + 0x7FFF + lsb) >> 16
+    r = (r << 16).astype(np.uint32)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = (x.view(np.uint32)[nan] | 0x00400000) & 0xFFFF0000
+    return r.view(np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """The 16-bit bfloat16 patterns of float32 values that are already bf16-exact."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return (u >> 16).astype(np.uint16)
+
+
+def round_to_f16(x: np.ndarray) -> np.ndarray:
+    """Round float32 to the nearest float16 (numpy's conversion is ties-to-even)."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
+def round_to(dtype: str, x: np.ndarray) -> np.ndarray:
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return round_to_bf16(x)
+    if dtype == "f16":
+        return round_to_f16(x)
+    raise ValueError(dtype)
+
+
+def make_inputs(w: Workload, *, N: Optional[int] = None, B: Optional[int] = None,
+                Hq: Optional[int] = None, Hkv: Optional[int] = None, d: Optional[int] = None):
+    """Draw (q, k, v) for workload ``w`` as float32 arrays whose values are exact
+    in ``w.dtype``.  Keyword overrides shrink the shape (same seed and recipe)."""
+    B = w.B if B is None else B
+    Hq = w.Hq if Hq is None else Hq
+    Hkv = w.Hkv if Hkv is None else Hkv
+    N = w.N if N is None else N
+    d = w.d if d is None else d
+    rng = np.random.default_rng(w.seed)
+    q = rng.standard_normal((B, Hq, N, d), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, N, d), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, N, d), dtype=np.float32)
+    if w.value_mult != 1.0:
+        m = np.float32(w.value_mult)
+        q *= m
+        k *= m
+        v *= m
+    if w.k_outlier_mult > 0.0 and d > 0:
+        c = int(rng.integers(d))
+        k[..., c] *= np.float32(w.k_outlier_mult)
+    return round_to(w.dtype, q), round_to(w.dtype, k), round_to(w.dtype, v)
+
+
+def random_inputs(seed: int, dtype: str, B: int, Hq: int, Hkv: int, N: int, d: int,
+                  mult: float = 1.0):
+    """Ad-hoc shapes for edge-case tests, same recipe as ``make_inputs``."""
+    w = Workload("adhoc", dtype, B, Hq, Hkv, N, d, False, -1, seed, value_mult=mult)
+    return make_inputs(w)
+
+
+def unmasked_pairs(N: int, causal: bool, window_left: int) -> int:
+    """Number of (query i, key j) pairs that a causal and/or left-window mask
+    keeps, per head: key j is kept when j <= i (if causal) and j >= i - wl
+    (if wl >= 0)."""
+    total = 0
+    if not causal and window_left < 0:
+        return N * N
+    i = np.arange(N, dtype=np.int64)
+    hi = i if causal else np.full(N, N - 1, dtype=np.int64)
+    lo = np.maximum(0, i - window_left) if window_left >= 0 else np.zeros(N, dtype=np.int64)
+    total = int(np.sum(hi - lo + 1))
+    return total
+
+
+def metric_flops(w: Workload) -> float:
+    """FLOPs credited to one forward call: 4*d per kept (query, key) pair per
+    head (2*d for the score, 2*d for the probability-weighted sum of V).
+    Causal without a window counts N^2/2 pairs (the usual convention); a window
+    counts the exact kept pairs."""
+    if w.causal and w.window_left < 0:
+        pairs = w.N * w.N / 2.0
+    else:
+        pairs = float(unmasked_pairs(w.N, w.causal, w.window_left))
+    return 4.0 * w.B * w.Hq * w.d * pairs
