@@ -1,0 +1,196 @@
+"""Attention-forward benchmark: TFLOP/s and fraction of the MI355X dense
+bf16/fp16 matrix-core peak.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload causal_8k]
+                    [--no-cpu-baseline] [--all] [--copy-calibration MiB]
+
+One step = one forward call (the whole path: Q/K/V tile staging, both
+contractions, online softmax, epilogue) over seeded synthetic inputs already
+resident in device memory.  Prints ONE JSON line (``--all``: one per
+workload, without the CPU baseline).
+
+FLOPs credited per call: 4*d per visible (query, key) pair per head; causal
+counts N^2/2 pairs, a window counts the exact visible pairs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense MFMA (fp32: vector/matrix)
+KERNEL_NAME = {"bf16": "fwd_mfma_kernel", "f16": "fwd_mfma_kernel", "f32": "fwd_f32_kernel"}
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP/C++ sources of libfa (sorted by name)."""
+    csrc = os.path.join(ROOT, "exact_tiled_attention_04_amd", "csrc")
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(csrc)):
+        if fn.endswith((".hip", ".cpp", ".h")):
+            h.update(fn.encode())
+            h.update(open(os.path.join(csrc, fn), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, budget_s: float = 12.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload:
+    every query row of successive (batch, head) slices, as many slices at a
+    time as there are host cores (one slice per worker thread, BLAS held to
+    one thread each), until ``budget_s`` of wall time has passed."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import workloads as W
+    from oracle import attention_fwd
+
+    cores = len(os.sched_getaffinity(0))
+    flops_per_head = W.metric_flops(w) / (w.B * w.Hq)
+    g = w.Hq // w.Hkv
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while done < len(heads) and time.perf_counter() - t0 < budget_s:
+            chunk = heads[done:done + cores]
+            qs = np.stack([q[b, h] for b, h in chunk])[None]
+            ks = np.stack([k[b, h // g] for b, h in chunk])[None]   # each query head's own K/V head
+            vs = np.stack([v[b, h // g] for b, h in chunk])[None]
+            attention_fwd(qs, ks, vs, w.causal, w.window_left, w.scale, threads=cores)
+            done += len(chunk)
+    dt = time.perf_counter() - t0
+    value = flops_per_head * done / dt / 1e12
+    return {"value": round(value, 6), "unit": "TFLOP/s", "cores": min(cores, len(heads)), "kind": "oracle",
+            "sample": f"{done} of {len(heads)} (batch, head) slices, all {w.N} query rows each, "
+                      f"fp64 numpy, {dt:.1f} s wall"}
+
+
+def run(args, name, with_cpu):
+    import numpy as np
+    import torch
+
+    import exact_tiled_attention_04_amd as fa
+    import workloads as W
+
+    w = W.WORKLOADS[name]
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    q, k, v = W.make_inputs(w)
+    qd, kd, vd = (torch.from_numpy(x).to(tdt).cuda() for x in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fa.fwd(qd, kd, vd, causal=w.causal, window_left=w.window_left, scale=w.scale,
+               out=o, lse=lse, stream=stream)
+
+    print(f"[bench] {name}: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    print(f"[bench] {name}: timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_ms = float(np.mean(per_launch_ms))
+    flops = W.metric_flops(w)
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = measured_traffic(name)
+    copy_note = None
+    if args.copy_calibration:
+        nbytes = args.copy_calibration * 2 ** 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        copy_note = f"copied {nbytes} bytes x3 for counter calibration"
+    rec = {
+        "metric": "attention fwd TFLOP/s + % of MI355X bf16 MFMA peak (d=128, causal, N=8k)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "window_left": w.window_left, "scale": w.scale,
+                   "seed": w.seed, "flops_per_step": flops},
+        "roofline": {"bound": "mfma" if w.dtype != "f32" else "alu", "achieved": round(achieved, 3),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "kernel": KERNEL_NAME[w.dtype],
+                     "avg_launch_us": round(avg_ms * 1e3, 2),
+                     "min_launch_us": round(float(np.min(per_launch_ms)) * 1e3, 2)},
+    }
+    if copy_note:
+        rec["calibration"] = copy_note
+    if with_cpu:
+        print(f"[bench] {name}: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v)
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="causal_8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true", help="one line per workload (no CPU baseline)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
+                    help="also run a device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the forward kernel runs on a single device "
+              "(multi-GPU sharding of batch x heads needs no communication and is not launched here).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.all:
+        import workloads as W
+        for name in W.ORDER:
+            print(json.dumps(run(args, name, False)), flush=True)
+        return
+    print(json.dumps(run(args, args.workload, not args.no_cpu_baseline)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,101 @@
+"""ctypes binding of libfa.so: the C entry points of include/fa.h under the
+same names, taking raw device addresses (ints) and sizes.
+
+Nothing here computes: each function marshals its arguments and calls the
+library.  If libfa.so has not been built, the first call raises; there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1, 2
+DTYPE_CODES = {"f32": FA_DTYPE_F32, "f16": FA_DTYPE_F16, "bf16": FA_DTYPE_BF16}
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_MISALIGNED = -3
+FA_ERR_HIP = -4
+
+EXPORTED = ["fa_fwd", "fa_fwd_bf16", "fa_fwd_f16", "fa_fwd_f32", "fa_status_string",
+            "fa_last_error", "fa_version"]
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A libfa call returned a negative status."""
+
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{fa_status_string(status)} ({status}): {detail}")
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m exact_tiled_attention_04_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        fwd_args = [P, P, P, P, P, I, I, I, I, I, I, I, F, P]
+        for name in ("fa_fwd_bf16", "fa_fwd_f16", "fa_fwd_f32"):
+            fn = getattr(lib, name)
+            fn.argtypes = fwd_args
+            fn.restype = I
+        lib.fa_fwd.argtypes = fwd_args + [I]
+        lib.fa_fwd.restype = I
+        lib.fa_status_string.argtypes = [I]
+        lib.fa_status_string.restype = ctypes.c_char_p
+        lib.fa_last_error.argtypes = []
+        lib.fa_last_error.restype = ctypes.c_char_p
+        lib.fa_version.argtypes = []
+        lib.fa_version.restype = I
+        _lib = lib
+    return _lib
+
+
+def _ptr(x):
+    return None if x is None or x == 0 else ctypes.c_void_p(int(x))
+
+
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window_left, scale, stream, dtype) -> int:
+    return load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
+                         int(bool(causal)), window_left, scale, _ptr(stream), dtype)
+
+
+def fa_fwd_bf16(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window_left, scale, stream) -> int:
+    return load().fa_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
+                              int(bool(causal)), window_left, scale, _ptr(stream))
+
+
+def fa_fwd_f16(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window_left, scale, stream) -> int:
+    return load().fa_fwd_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
+                             int(bool(causal)), window_left, scale, _ptr(stream))
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window_left, scale, stream) -> int:
+    return load().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
+                             int(bool(causal)), window_left, scale, _ptr(stream))
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(status).decode()
+
+
+def fa_last_error() -> str:
+    return load().fa_last_error().decode()
+
+
+def fa_version() -> int:
+    return load().fa_version()

@@ -1,0 +1,58 @@
+"""torch-facing wrapper over the C ABI: torch supplies device memory and the
+current stream; every step of the computation runs in libfa's HIP kernels."""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.FA_DTYPE_F32, torch.float16: _lib.FA_DTYPE_F16,
+           torch.bfloat16: _lib.FA_DTYPE_BF16}
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+        window_left: int = -1, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+        lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+        stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Exact attention forward on the GPU.
+
+    q: [B, Hq, N, d]; k, v: [B, Hkv, N, d]; contiguous, one dtype (float32,
+    float16 or bfloat16), on one GPU.  Returns (o, lse): o like q, lse float32
+    [B, Hq, N] (None when want_lse is False and no lse buffer is given).
+    The call is asynchronous on ``stream`` (default: the current stream).
+    Raises _lib.FaError when the library rejects the arguments.
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError(f"q, k, v must share one dtype of {list(_DTYPES)}")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on one GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, Hq, N, d = q.shape
+    if tuple(k.shape) != (B, k.shape[1], N, d) or k.shape != v.shape:
+        raise ValueError("k and v must be [B, Hkv, N, d] with q's B, N, d")
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = out if out is not None else torch.empty_like(q)
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, Hq, N) or lse.dtype != torch.float32
+                            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, N] tensor")
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        status = _lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             lse.data_ptr() if lse is not None else None,
+                             B, Hq, Hkv, N, d, causal, window_left, float(scale), s.cuda_stream,
+                             _DTYPES[q.dtype])
+    if status != _lib.FA_OK:
+        raise _lib.FaError(status, _lib.fa_last_error())
+    return o, lse

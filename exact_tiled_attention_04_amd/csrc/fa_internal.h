@@ -1,0 +1,104 @@
+// Internal declarations shared by the C-ABI wrapper and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace fa {
+
+// Validated arguments of one forward call (sizes already checked on the host).
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // may be null: skip writing the logsumexp
+  int B, Hq, Hkv, N, d;
+  int causal;
+  int window_left;  // -1 = no window
+  float scale;      // > 0
+};
+
+// Kernel-side copy of the arguments plus derived constants.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, N;
+  int group;         // Hq / Hkv: query heads per key/value head
+  int causal;
+  int window_left;
+  int n_qblocks;     // ceil(N / rows per workgroup)
+  int total_items;   // B * Hq * n_qblocks
+  float scale_log2;  // scale * log2(e): scores go straight into exp2
+};
+
+// Workgroup -> (batch*head, query block) mapping.
+//
+// Workgroups are handed to the 8 XCDs of the chip round-robin (workgroup id
+// modulo 8), and each XCD has its own L2.  The mapping gives every XCD a
+// contiguous slice of a logical order in which the query blocks of the query
+// heads that share one key/value head are adjacent, so the K/V tiles that
+// those workgroups stream are shared through one L2.  With a causal mask the
+// logical order within a head group runs from the last query block (the most
+// key tiles) to the first, so long workgroups start early.
+struct WorkItem {
+  int bh;  // b * Hq + query head
+  int qb;  // query block index
+};
+
+__device__ __forceinline__ WorkItem decode_work_item(const FwdParams& p, int id) {
+  constexpr int NXCD = 8;
+  const int xcd = id % NXCD;
+  const int r = id / NXCD;
+  const int per = p.total_items / NXCD;
+  const int rem = p.total_items % NXCD;
+  const int L = xcd * per + (xcd < rem ? xcd : rem) + r;
+  const int per_group = p.group * p.n_qblocks;
+  const int gidx = L / per_group;
+  const int w = L - gidx * per_group;
+  const int qrank = w / p.group;
+  const int hg = w - qrank * p.group;
+  const int b = gidx / p.Hkv;
+  const int hk = gidx - b * p.Hkv;
+  WorkItem it;
+  it.bh = b * p.Hq + hk * p.group + hg;
+  it.qb = p.causal ? (p.n_qblocks - 1 - qrank) : qrank;
+  return it;
+}
+
+inline FwdParams make_params(const FwdArgs& a, int rows_per_wg) {
+  FwdParams p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.B = a.B;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.N = a.N;
+  p.group = a.Hq / a.Hkv;
+  p.causal = a.causal ? 1 : 0;
+  // a window of N-1 or more keys reaches back past key 0 and hides nothing
+  p.window_left = (a.window_left >= a.N - 1) ? -1 : a.window_left;
+  p.n_qblocks = (a.N + rows_per_wg - 1) / rows_per_wg;
+  p.total_items = a.B * a.Hq * p.n_qblocks;
+  p.scale_log2 = a.scale * 1.4426950408889634f;
+  return p;
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+
+// Query rows handled by one workgroup of each kernel.
+long long mfma_rows_per_workgroup();
+long long f32_rows_per_workgroup();
+
+// Largest B*Hq*n_qblocks a single launch accepts (grid.x limit).
+constexpr long long kMaxGridItems = 2147483647LL;
+
+}  // namespace fa

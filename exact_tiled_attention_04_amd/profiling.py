@@ -1,0 +1,161 @@
+"""Summarise rocprofv3 output for the attention kernel into short text/JSON
+files under ``profiles/``.
+
+    python -m exact_tiled_attention_04_amd.profiling \\
+        --workload causal_8k --trace DIR [--fetch DIR --write DIR --copy-mib 1024] \\
+        [--pmc DIR ...] --command "..." [--last N]
+
+--trace   a ``rocprofv3 --kernel-trace --stats`` output directory
+--fetch / --write
+          ``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` output
+          directories of a run that also copied ``--copy-mib`` MiB device to
+          device; the copy's own counter value (bytes known) calibrates the
+          counter: bytes = counter_KiB * 1024 * (copy bytes / copy counter bytes)
+--pmc     further counter-collection directories (SQ_*/GRBM_* counters), summed
+          per dispatch of the attention kernel
+--last    use only the last N dispatches of the kernel (the timed steps)
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_KEY = "fwd_"
+
+
+def kernel_source_hash() -> str:
+    csrc = os.path.join(ROOT, "exact_tiled_attention_04_amd", "csrc")
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(csrc)):
+        if fn.endswith((".hip", ".cpp", ".h")):
+            h.update(fn.encode())
+            h.update(open(os.path.join(csrc, fn), "rb").read())
+    return h.hexdigest()
+
+
+def _csv(d, suffix):
+    files = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return list(csv.DictReader(open(files[0])))
+
+
+def _is_attn(name):
+    return KERNEL_KEY in name and "fa::" in name
+
+
+def trace_summary(d, last=None):
+    rows = [r for r in _csv(d, "kernel_trace.csv") if _is_attn(r["Kernel_Name"])]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in rows]
+    if last:
+        durs = durs[-last:]
+    return {"kernel": rows[0]["Kernel_Name"] if rows else None, "dispatches": len(durs),
+            "avg_us": statistics.mean(durs) / 1e3 if durs else None,
+            "min_us": min(durs) / 1e3 if durs else None, "max_us": max(durs) / 1e3 if durs else None,
+            "grid": rows[0].get("Grid_Size_X") if rows else None,
+            "workgroup": rows[0].get("Workgroup_Size_X") if rows else None,
+            "lds_bytes": rows[0].get("LDS_Block_Size") if rows else None,
+            "vgpr": rows[0].get("VGPR_Count") if rows else None,
+            "agpr": rows[0].get("Accum_VGPR_Count") if rows else None}
+
+
+def counter_per_dispatch(d, last=None):
+    """{counter: [value per dispatch]} for the attention kernel, plus the copy kernel."""
+    rows = _csv(d, "counter_collection.csv")
+    attn, copy = {}, {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        target = attn if _is_attn(name) else copy if "copyBuffer" in name else None
+        if target is None:
+            continue
+        key = (r["Dispatch_Id"], r["Counter_Name"])
+        target[key] = target.get(key, 0.0) + float(r["Counter_Value"])
+    def regroup(m):
+        out = {}
+        for (disp, cname), val in sorted(m.items(), key=lambda kv: int(kv[0][0])):
+            out.setdefault(cname, []).append(val)
+        return out
+    a = regroup(attn)
+    if last:
+        a = {k: v[-last:] for k, v in a.items()}
+    return a, regroup(copy)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-mib", type=int, default=0)
+    ap.add_argument("--pmc", nargs="*", default=[])
+    ap.add_argument("--command", action="append", default=[])
+    ap.add_argument("--last", type=int, default=None)
+    ap.add_argument("--flops", type=float, default=None, help="algorithmic FLOPs per launch")
+    ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
+    args = ap.parse_args()
+
+    tr = trace_summary(args.trace, args.last)
+    lines = [f"# attention forward kernel, workload {args.workload}", "",
+             "Commands (run from the repository root on one MI355X):", ""]
+    lines += [f"    {c}" for c in args.command]
+    lines += ["", f"kernel: `{tr['kernel']}`",
+              f"grid {tr['grid']} work-items, workgroup {tr['workgroup']}, LDS {tr['lds_bytes']} B, "
+              f"VGPR {tr['vgpr']}, AGPR {tr['agpr']}", "",
+              f"kernel trace, last {tr['dispatches']} dispatches: avg {tr['avg_us']:.1f} us, "
+              f"min {tr['min_us']:.1f} us, max {tr['max_us']:.1f} us"]
+    if args.flops:
+        lines.append(f"algorithmic FLOPs per launch {args.flops:.4e} -> {args.flops / (tr['avg_us'] * 1e-6) / 1e12:.1f} "
+                     f"TFLOP/s at the average duration ({100 * args.flops / (tr['avg_us'] * 1e-6) / 2516.6e12:.1f}% "
+                     f"of 2516.6 TFLOP/s)")
+    traffic = None
+    if args.fetch and args.write and args.copy_mib:
+        copy_bytes = args.copy_mib * 2 ** 20
+        fa_f, cp_f = counter_per_dispatch(args.fetch, args.last)
+        fa_w, cp_w = counter_per_dispatch(args.write, args.last)
+        f_scale = copy_bytes / (statistics.mean(cp_f["FETCH_SIZE"]) * 1024)
+        w_scale = copy_bytes / (statistics.mean(cp_w["WRITE_SIZE"]) * 1024)
+        fetch_b = statistics.mean(fa_f["FETCH_SIZE"]) * 1024 * f_scale
+        write_b = statistics.mean(fa_w["WRITE_SIZE"]) * 1024 * w_scale
+        traffic = fetch_b + write_b
+        lines += ["", "HBM traffic per launch (counters in KiB per dispatch, scaled by a device copy of "
+                  f"{args.copy_mib} MiB measured in the same run):",
+                  f"  FETCH_SIZE: copy reads {statistics.mean(cp_f['FETCH_SIZE']):.0f} KiB for "
+                  f"{copy_bytes // 1024} KiB -> factor {f_scale:.4f}; kernel {statistics.mean(fa_f['FETCH_SIZE']):.0f} KiB "
+                  f"-> {fetch_b / 2**20:.1f} MiB read",
+                  f"  WRITE_SIZE: copy writes {statistics.mean(cp_w['WRITE_SIZE']):.0f} KiB for "
+                  f"{copy_bytes // 1024} KiB -> factor {w_scale:.4f}; kernel {statistics.mean(fa_w['WRITE_SIZE']):.0f} KiB "
+                  f"-> {write_b / 2**20:.1f} MiB written",
+                  f"  total {traffic / 2**20:.1f} MiB per launch"]
+        json.dump({"workload": args.workload, "kernel_source_sha256": kernel_source_hash(),
+                   "hbm_bytes_per_launch": round(traffic), "fetch_bytes": round(fetch_b),
+                   "write_bytes": round(write_b), "fetch_scale": f_scale, "write_scale": w_scale,
+                   "commands": args.command},
+                  open(os.path.join(args.out_dir, f"traffic_{args.workload}.json"), "w"), indent=1)
+    for d in args.pmc:
+        a, _ = counter_per_dispatch(d, args.last)
+        lines += ["", f"counters ({os.path.basename(os.path.normpath(d))}), mean per dispatch:"]
+        for k, v in sorted(a.items()):
+            lines.append(f"  {k:34s} {statistics.mean(v):.6g}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in a and "GRBM_GUI_ACTIVE" in a:
+            simd = 256 * 4
+            util = statistics.mean(a["SQ_VALU_MFMA_BUSY_CYCLES"]) / (statistics.mean(a["GRBM_GUI_ACTIVE"]) * simd)
+            lines.append(f"  MFMA busy / (GUI active x 1024 SIMDs) = {100 * util:.1f}%")
+        if "SQ_LDS_BANK_CONFLICT" in a and "SQ_LDS_IDX_ACTIVE" in a:
+            bc = statistics.mean(a["SQ_LDS_BANK_CONFLICT"]) / max(1.0, statistics.mean(a["SQ_LDS_IDX_ACTIVE"]))
+            lines.append(f"  LDS bank-conflict cycles / LDS active cycles = {100 * bc:.2f}%")
+    lines.append(f"\nkernel sources sha256 {kernel_source_hash()}")
+    out = os.path.join(args.out_dir, f"fwd_{args.workload}.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,121 @@
+/*
+ * fa.h -- exact attention forward for AMD MI355X (gfx950), C ABI.
+ *
+ * Operation (one call):  for every batch b, query head h and query row i,
+ *
+ *     s_ij   = scale * sum_c q[b][h][i][c] * k[b][g(h)][j][c]
+ *     s_ij   = -inf                       where (i, j) is masked
+ *     o[b][h][i][:] = sum_j softmax_j(s_i.) * v[b][g(h)][j][:]
+ *     lse[b][h][i]  = log( sum_j exp(s_ij) )          (natural log)
+ *
+ * with g(h) = h / (Hq / Hkv) (consecutive groups of query heads share one
+ * key/value head) and (i, j) masked when (causal && j > i) or
+ * (window_left >= 0 && j < i - window_left).
+ *
+ * This is standard attention, softmax(Q K^T) V, as drawn in the "AS-IS"
+ * diagram of the Flash Attention page (heepie.pages.dev), computed the IO-aware
+ * way of that page's "TO-BE" diagram and tiling section: K/V tiles are staged
+ * on chip, the N x N score matrix never reaches device memory, and an online
+ * softmax (FlashAttention quiz, question 4) rescales a running partial result.
+ * The mask and the GQA head sharing follow the Hacker News answer on GQA and
+ * sliding windows (a window only changes the mask; GQA only changes which K/V
+ * head a query head reads).  The scale, the causal convention (key j visible
+ * to query i iff j <= i), the window convention (window_left keys before the
+ * query stay visible, plus the query's own key) and the logsumexp output are
+ * this library's readings of points the pages leave open.
+ *
+ * Layout (all contiguous, row-major, element type given by the dtype):
+ *     q, o : [B][Hq][N][d]          k, v : [B][Hkv][N][d]
+ *     lse  : [B][Hq][N] float32
+ * o has the element type of q.  d is the fastest axis.
+ *
+ * Ownership and execution:
+ *   - Every pointer is device memory on the current HIP device, allocated and
+ *     owned by the caller.  q, k and v are only read and may alias each other;
+ *     o and lse are only written and must not overlap any input or each other.
+ *   - The library allocates no device memory and keeps no per-call state; all
+ *     entry points are thread-safe.
+ *   - The call is asynchronous: it validates its arguments on the host,
+ *     enqueues the work on `stream` (a hipStream_t; NULL = the null stream)
+ *     and returns.  It never synchronises.  Faults inside the kernel surface at
+ *     the caller's next synchronisation, as for any HIP launch.
+ *   - Results are deterministic: the same inputs give bit-identical o and lse.
+ *
+ * Errors: every argument is checked on the host before anything is enqueued;
+ * on failure the call returns a negative fa_status_t, writes nothing, and
+ * fa_last_error() (thread-local) describes the problem.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_DTYPE_F32 = 0,   /* IEEE binary32 */
+  FA_DTYPE_F16 = 1,   /* IEEE binary16 */
+  FA_DTYPE_BF16 = 2   /* bfloat16 */
+} fa_dtype_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null pointer, negative size, Hq % Hkv != 0,
+                              window_left < -1, non-finite scale          */
+  FA_ERR_UNSUPPORTED = -2, /* d not 64 or 128, unknown dtype, scale <= 0,
+                              a size whose offsets overflow 64 bits       */
+  FA_ERR_MISALIGNED = -3,  /* q, k, v or o not 16-byte aligned, lse not
+                              4-byte aligned                              */
+  FA_ERR_HIP = -4          /* the HIP runtime reported an error at launch */
+} fa_status_t;
+
+/*
+ * Attention forward for element type `dtype`.
+ *
+ *   q, k, v      inputs (device), layouts above.
+ *   o            output (device), same element type and layout as q.
+ *   lse          output (device) float32 [B][Hq][N], or NULL to skip it.
+ *   B, Hq, Hkv   batch size, query heads, key/value heads (Hq % Hkv == 0).
+ *   N            sequence length (queries and keys alike).
+ *   d            head dimension: 64 or 128.
+ *   causal       nonzero: key j is hidden from query i when j > i.
+ *   window_left  -1: no window.  >= 0: key j is hidden from query i when
+ *                j < i - window_left.  Composes with `causal`.
+ *   scale        multiplier on q.k before the softmax; finite and > 0
+ *                (the usual value is 1/sqrt(d)).
+ *   stream       hipStream_t to enqueue on, NULL for the null stream.
+ *
+ * If B, Hq or N is 0 the call does nothing and returns FA_OK (pointers are
+ * then not inspected).  Otherwise Hkv must be >= 1.
+ * Returns FA_OK or a negative fa_status_t.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int Hq, int Hkv, int N, int d, int causal, int window_left,
+           float scale, void *stream, fa_dtype_t dtype);
+
+/* The same operation with the element type fixed by the name. */
+int fa_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
+                int B, int Hq, int Hkv, int N, int d, int causal, int window_left,
+                float scale, void *stream);
+int fa_fwd_f16(const void *q, const void *k, const void *v, void *o, float *lse,
+               int B, int Hq, int Hkv, int N, int d, int causal, int window_left,
+               float scale, void *stream);
+int fa_fwd_f32(const void *q, const void *k, const void *v, void *o, float *lse,
+               int B, int Hq, int Hkv, int N, int d, int causal, int window_left,
+               float scale, void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *fa_status_string(int status);
+
+/* Detail of this thread's last failing call ("" if none).  The pointer stays
+ * valid until this thread's next call into the library. */
+const char *fa_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

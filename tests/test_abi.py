@@ -1,0 +1,108 @@
+"""CPU tests of the C ABI: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host with the documented
+status, before any device work (no call here reaches a kernel launch)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_tiled_attention_04_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libfa.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_documented_entry_points():
+    assert declared_functions() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    assert _lib.fa_status_string(0) == "FA_OK"
+    assert _lib.fa_status_string(-1) == "FA_ERR_INVALID_ARG"
+    assert _lib.fa_status_string(-2) == "FA_ERR_UNSUPPORTED"
+    assert _lib.fa_status_string(-3) == "FA_ERR_MISALIGNED"
+    assert _lib.fa_status_string(-4) == "FA_ERR_HIP"
+    assert _lib.fa_status_string(7) == "FA_UNKNOWN_STATUS"
+    assert _lib.fa_version() >= 100
+
+
+# Fake, well-aligned, non-overlapping "device addresses": every case below
+# fails validation before the library touches them.
+Q, K, V, O, L = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+GOOD = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, Hq=4, Hkv=2, N=16, d=64, causal=0,
+            window_left=-1, scale=0.125, stream=None)
+
+
+def call(dtype=_lib.FA_DTYPE_BF16, **over):
+    a = dict(GOOD, **over)
+    return _lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["N"],
+                       a["d"], a["causal"], a["window_left"], a["scale"], a["stream"], dtype)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(B=-1), _lib.FA_ERR_INVALID_ARG),
+    (dict(N=-5), _lib.FA_ERR_INVALID_ARG),
+    (dict(Hkv=-1), _lib.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), _lib.FA_ERR_INVALID_ARG),
+    (dict(Hkv=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(Hkv=8), _lib.FA_ERR_INVALID_ARG),
+    (dict(window_left=-2), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), _lib.FA_ERR_UNSUPPORTED),
+    (dict(scale=-0.5), _lib.FA_ERR_UNSUPPORTED),
+    (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
+    (dict(d=256), _lib.FA_ERR_UNSUPPORTED),
+    (dict(q=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(o=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(q=Q + 8), _lib.FA_ERR_MISALIGNED),
+    (dict(o=O + 2), _lib.FA_ERR_MISALIGNED),
+    (dict(lse=L + 2), _lib.FA_ERR_MISALIGNED),
+    (dict(o=Q), _lib.FA_ERR_INVALID_ARG),          # output aliases an input
+    (dict(lse=O + 64), _lib.FA_ERR_INVALID_ARG),   # lse inside o
+])
+def test_validation_rejects(over, status):
+    assert call(**over) == status
+    assert _lib.fa_last_error() != ""
+
+
+def test_unknown_dtype():
+    assert call(dtype=7) == _lib.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("over", [dict(B=0), dict(Hq=0), dict(N=0), dict(B=0, q=0, k=0, v=0, o=0, lse=0)])
+def test_empty_problem_is_a_noop(over):
+    assert call(**over) == _lib.FA_OK
+    assert _lib.fa_last_error() == ""
+
+
+def test_typed_entry_points_validate_too():
+    for fn in (_lib.fa_fwd_bf16, _lib.fa_fwd_f16, _lib.fa_fwd_f32):
+        assert fn(Q, K, V, O, L, 1, 4, 3, 16, 64, 0, -1, 0.1, None) == _lib.FA_ERR_INVALID_ARG
+        assert fn(Q, K, V, O, L, 1, 4, 2, 16, 80, 0, -1, 0.1, None) == _lib.FA_ERR_UNSUPPORTED
+        assert fn(0, 0, 0, 0, 0, 0, 4, 2, 16, 64, 0, -1, 0.1, None) == _lib.FA_OK
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load()
