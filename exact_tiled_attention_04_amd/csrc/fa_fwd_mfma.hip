@@ -42,6 +42,8 @@
 // (v_permlane32_swap) and the rescale and 1/l are per-lane scalars.
 #include "fa_internal.h"
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
@@ -87,28 +89,41 @@ struct F16 {
 
 template <int D>
 struct Shape {
-  static constexpr int kChunks = D / 8;    // 16-byte chunks per row
-  static constexpr int kSteps = D / 16;    // MFMA k-steps over the head dimension
-  static constexpr int kOutTiles = D / 32; // 32-wide output channel tiles
-  static constexpr int kChunksPerThread = kBC * kChunks / kThreads;
-  static_assert(kBC * kChunks % kThreads == 0, "tile must split evenly over the workgroup");
+  static constexpr int kChunks = D / 8;     // 16-byte chunks per row
+  static constexpr int kSteps = D / 16;     // MFMA k-steps over the head dimension
+  static constexpr int kOutTiles = D / 32;  // 32-wide output channel tiles
+  static constexpr int kRowBytes = 2 * D;
+  // one wave-wide 16-byte-per-lane load moves 1 KiB = this many rows
+  static constexpr int kRowsPerLoad = 1024 / kRowBytes;
+  static constexpr int kLoadsPerWave = kBC / kRowsPerLoad / kWaves;
+  static_assert(kBC % (kRowsPerLoad * kWaves) == 0, "tile must split evenly over the wavefronts");
 };
 
-// LDS layouts.  Both tiles are row-major [key][dim] with 16-byte chunks
-// permuted within a row by an XOR of the row index:
-//   K: chunk ^ (row mod chunks-per-row).  A K read has the 32 lanes of a half
-//      wave on 32 consecutive rows at one logical chunk; the XOR spreads any
-//      16 consecutive rows over all chunk positions (all banks).
-//   V: chunk ^ 2*(row mod 4).  A transposing read has each 16-lane group on 4
-//      consecutive rows x 32 bytes; the XOR puts those 4 rows' 32-byte pieces
-//      in distinct banks.
+// LDS layouts.  Both tiles are row-major [key][dim]; the 16-byte chunks of a
+// row are permuted by an XOR with a function of the row, chosen (by bank-
+// conflict counts on gfx950, whose LDS serves 256 bytes per clock) so that the
+// reads of the hot loop are conflict-free:
+//   K, read 16 bytes per lane with the 32 lanes of a half-wave on 32
+//     consecutive rows: D=128 chunk ^ (row mod 16); D=64 (two rows per 256
+//     bytes) chunk ^ ((row / 2) mod 8).
+//   V, read through the transposing load with each 16-lane group on 4
+//     consecutive rows x 32 bytes: D=128 chunk ^ 4*(row mod 4); D=64
+//     chunk ^ 2*(row mod 4).
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  return D == 128 ? ((row & 3) << 2) : ((row & 3) << 1);
+}
 template <int D>
 __device__ __forceinline__ int k_off(int row, int chunk) {
-  return row * D + ((chunk ^ (row & (Shape<D>::kChunks - 1))) << 3);
+  return row * D + ((chunk ^ k_swz<D>(row)) << 3);
 }
 template <int D>
 __device__ __forceinline__ int v_off(int row, int col) {
-  return row * D + ((((col >> 3) ^ ((row & 3) << 1))) << 3) + (col & 7);
+  return row * D + (((col >> 3) ^ v_swz<D>(row)) << 3) + (col & 7);
 }
 
 // Exchange with the lane 32 away: returns the pair in a fixed order (lower
@@ -119,192 +134,242 @@ __device__ __forceinline__ void half_pair(float x, float& lo, float& hi) {
   hi = __uint_as_float(r[1]);
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
 __device__ __forceinline__ s16x4 lds_read_tr(const unsigned short* base, int off) {
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
 }
 
+// Start the copy of key tile [kb, kb + kBC) of K and V from device memory
+// straight into LDS (buffer loads with the LDS destination; no registers).
+// Each wave moves kLoadsPerWave 1-KiB pieces of each tensor: lane l fills LDS
+// bytes 16l..16l+15 of its piece, so it fetches the logical chunk that the
+// swizzle maps there.  Rows past the end of the sequence are outside the
+// buffer's range and arrive as zeros.
+template <int D>
+__device__ __forceinline__ void load_tile_async(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                                unsigned short* sk, unsigned short* sv, int kb,
+                                                int wave, int lane) {
+  using S = Shape<D>;
+#pragma unroll
+  for (int u = 0; u < S::kLoadsPerWave; ++u) {
+    const int piece = wave * S::kLoadsPerWave + u;
+    const int row = piece * S::kRowsPerLoad + lane / S::kChunks;
+    const int pch = lane % S::kChunks;  // physical chunk this lane fills
+    const int gk = (kb + row) * S::kRowBytes + ((pch ^ k_swz<D>(row)) << 4);
+    const int gv = (kb + row) * S::kRowBytes + ((pch ^ v_swz<D>(row)) << 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(sk + piece * 512), 16, gk, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(sv + piece * 512), 16, gv, 0, 0, 0);
+  }
+}
+
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
+
+// Per-lane constants of one workgroup's key loop.
+struct LoopCtx {
+  __amdgpu_buffer_rsrc_t rk, rv;  // this (batch, kv head)'s K and V, bounded to N rows
+  int N, wl, t_end;
+  int wave, lane, l32, hh;
+  int wq0, wq1;                   // first and last valid row of the wavefront
+  int vis_lo;                     // first visible key of this lane's row
+  unsigned vis_span;              // visible keys: vis_lo .. vis_lo + vis_span
+  int v_row_lane, v_col_lane;     // lane geometry of the transposing V read
+  bool causal;
+  float c;                        // scale * log2(e)
+};
+
+// Running state of the lane's query row.
+template <int D>
+struct RowState {
+  u32x4 qf[Shape<D>::kSteps];         // q row as the B operand
+  f32x16 oacc[Shape<D>::kOutTiles];   // unnormalised O^T columns
+  float m_run;                        // running max of scale*log2(e)*score
+  float l_run;                        // running sum of exp2(. - m_run), this half-wave's keys
+};
+
+// One key tile: start the copy of tile t+1 into the other buffers, then
+// fold tile t (already in cK/cV) into the row state.  The buffer pointers
+// are restrict-qualified: the copies into nK/nV never touch cK/cV, which lets
+// the LDS reads below proceed while those copies are in flight.
+template <typename E, int D>
+__device__ __forceinline__ void tile_step(const unsigned short* __restrict__ cK,
+                                          const unsigned short* __restrict__ cV,
+                                          unsigned short* __restrict__ nK,
+                                          unsigned short* __restrict__ nV, const LoopCtx& x,
+                                          RowState<D>& st, int t) {
+  using S = Shape<D>;
+  if (t + 1 < x.t_end) load_tile_async<D>(x.rk, x.rv, nK, nV, (t + 1) * kBC, x.wave, x.lane);
+
+  const int kb = t * kBC;
+  const int ke = kb + kBC - 1;
+  const bool skip = (x.wq0 >= x.N) || (x.causal && kb > x.wq1) || (x.wl >= 0 && ke < x.wq0 - x.wl);
+  if (skip) return;
+  const bool need_mask = (ke >= x.N) || (x.causal && ke > x.wq0) || (x.wl >= 0 && kb < x.wq1 - x.wl);
+
+  // ---- scores: S^T = K Q^T, keys kb..kb+31 in s0 and kb+32..kb+63 in s1
+  f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+  for (int kc = 0; kc < S::kSteps; ++kc) {
+    const u32x4 a0 = *(const u32x4*)(cK + k_off<D>(x.l32, 2 * kc + x.hh));
+    const u32x4 a1 = *(const u32x4*)(cK + k_off<D>(32 + x.l32, 2 * kc + x.hh));
+    s0 = E::mma(a0, st.qf[kc], s0);
+    s1 = E::mma(a1, st.qf[kc], s1);
+  }
+
+  // ---- mask (tiles crossing the diagonal, the window edge or the end):
+  // key kb + off is visible iff 0 <= kb + off - vis_lo <= vis_span
+  if (need_mask) {
+    const int base = kb - x.vis_lo + 4 * x.hh;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int off = 8 * (i >> 2) + (i & 3);
+      s0[i] = ((unsigned)(base + off) <= x.vis_span) ? s0[i] : -INFINITY;
+      s1[i] = ((unsigned)(base + off + 32) <= x.vis_span) ? s1[i] : -INFINITY;
+    }
+  }
+
+  // ---- online softmax (base 2, scale folded into the exponent)
+  float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+  float mlo, mhi;
+  half_pair(mx, mlo, mhi);
+  mx = fmaxf(mlo, mhi);
+  const float m_new = fmaxf(st.m_run, mx * x.c);
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // nothing visible yet
+  const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_use);
+  st.m_run = m_new;
+  float rs = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], x.c, -m_use));
+    s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], x.c, -m_use));
+    rs += s0[i] + s1[i];
+  }
+  st.l_run = st.l_run * alpha + rs;
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+    for (int ct = 0; ct < S::kOutTiles; ++ct) st.oacc[ct] *= alpha;
+  }
+
+  // ---- P^T operands: the lane's own probabilities, 8 keys per k-step
+  u32x4 pf[4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    pf[j] = u32x4{E::pack2(s0[8 * j + 0], s0[8 * j + 1]), E::pack2(s0[8 * j + 2], s0[8 * j + 3]),
+                  E::pack2(s0[8 * j + 4], s0[8 * j + 5]), E::pack2(s0[8 * j + 6], s0[8 * j + 7])};
+    pf[2 + j] = u32x4{E::pack2(s1[8 * j + 0], s1[8 * j + 1]), E::pack2(s1[8 * j + 2], s1[8 * j + 3]),
+                      E::pack2(s1[8 * j + 4], s1[8 * j + 5]), E::pack2(s1[8 * j + 6], s1[8 * j + 7])};
+  }
+
+  // ---- O^T += V^T P^T.  k-step mc covers keys 16mc..16mc+15 in the order
+  // the accumulator hands them over: half-wave hh holds keys
+  // 16mc + 4hh + {0..3} and 16mc + 8 + 4hh + {0..3}.
+#pragma unroll
+  for (int ct = 0; ct < S::kOutTiles; ++ct) {
+    const int col = 32 * ct + x.v_col_lane;
+#pragma unroll
+    for (int mc = 0; mc < 4; ++mc) {
+      const int ra = 16 * mc + x.v_row_lane;
+      const s16x4 lo = lds_read_tr(cV, v_off<D>(ra, col));
+      const s16x4 hi = lds_read_tr(cV, v_off<D>(ra + 8, col));
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+      const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 a = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+      st.oacc[ct] = E::mma(a, pf[mc], st.oacc[ct]);
+    }
+  }
+}
+
 template <typename E, int D>
 __global__ void __launch_bounds__(kThreads, 2) fwd_mfma_kernel(FwdParams p) {
   using S = Shape<D>;
-  __shared__ __attribute__((aligned(16))) unsigned short sK[kBC * D];
-  __shared__ __attribute__((aligned(16))) unsigned short sV[kBC * D];
+  // two K/V buffers as separate objects
+  __shared__ __attribute__((aligned(16))) unsigned short sK0[kBC * D];
+  __shared__ __attribute__((aligned(16))) unsigned short sV0[kBC * D];
+  __shared__ __attribute__((aligned(16))) unsigned short sK1[kBC * D];
+  __shared__ __attribute__((aligned(16))) unsigned short sV1[kBC * D];
 
+  LoopCtx x;
   const int tid = threadIdx.x;
-  const int lane = tid & (kWaveSize - 1);
-  const int wave = tid / kWaveSize;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;  // which half-wave
+  x.lane = tid & (kWaveSize - 1);
+  x.wave = tid / kWaveSize;
+  x.l32 = x.lane & 31;
+  x.hh = x.lane >> 5;
 
   const WorkItem it = decode_work_item(p, blockIdx.x);
   const int N = p.N;
+  x.N = N;
   const int b = it.bh / p.Hq;
   const int hq = it.bh - b * p.Hq;
   const int hk = hq / p.group;
   const long long q_head = (long long)it.bh * N * D;
   const long long kv_head = ((long long)b * p.Hkv + hk) * N * D;
   const unsigned short* __restrict__ qg = (const unsigned short*)p.q + q_head;
-  const unsigned short* __restrict__ kg = (const unsigned short*)p.k + kv_head;
-  const unsigned short* __restrict__ vg = (const unsigned short*)p.v + kv_head;
+  const int head_bytes = N * S::kRowBytes;
+  x.rk = __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned short*)p.k + kv_head), 0, head_bytes,
+                                           kBufferFlags);
+  x.rv = __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned short*)p.v + kv_head), 0, head_bytes,
+                                           kBufferFlags);
 
-  const bool causal = p.causal != 0;
-  const int wl = p.window_left;
+  x.causal = p.causal != 0;
+  x.wl = p.window_left;
+  x.c = p.scale_log2;
   const int q0 = it.qb * kBR;
-  const int wq0 = q0 + wave * kRowsPerWave;          // first row of this wavefront
-  const int wq1 = min(N, wq0 + kRowsPerWave) - 1;    // last valid row (< wq0 if none)
-  const int myq = wq0 + l32;                         // this lane's query row
+  x.wq0 = q0 + x.wave * kRowsPerWave;
+  x.wq1 = min(N, x.wq0 + kRowsPerWave) - 1;
+  const int myq = x.wq0 + x.l32;  // this lane's query row
 
   // Key tiles this workgroup needs: causal stops at its last row, a window
   // starts window_left keys before its first row.
-  const int kend = causal ? min(N, q0 + kBR) : N;
-  const int kbeg = wl >= 0 ? max(0, q0 - wl) : 0;
+  const int kend = x.causal ? min(N, q0 + kBR) : N;
+  const int kbeg = x.wl >= 0 ? max(0, q0 - x.wl) : 0;
   const int t_beg = kbeg / kBC;
-  const int t_end = (kend + kBC - 1) / kBC;
+  x.t_end = (kend + kBC - 1) / kBC;
 
-  // Q as the B operand: q[myq][16*kc + 8*hh .. +7] for each k-step kc.
-  u32x4 qf[S::kSteps];
+  // Visible keys of this lane's row form one range [vis_lo, vis_lo + vis_span].
+  x.vis_lo = x.wl >= 0 ? max(0, myq - x.wl) : 0;
+  const int vis_hi = x.causal ? min(myq, N - 1) : N - 1;
+  x.vis_span = (unsigned)(vis_hi - x.vis_lo);
+
+  const int g16 = x.lane >> 4;
+  const int gi = x.lane & 15;
+  x.v_row_lane = 4 * x.hh + (gi >> 2);
+  x.v_col_lane = 16 * (g16 & 1) + 4 * (gi & 3);
+
+  if (t_beg < x.t_end) load_tile_async<D>(x.rk, x.rv, sK0, sV0, t_beg * kBC, x.wave, x.lane);
+
+  RowState<D> st;
 #pragma unroll
   for (int kc = 0; kc < S::kSteps; ++kc) {
     if (myq < N)
-      qf[kc] = *(const u32x4*)(qg + (long long)myq * D + 16 * kc + 8 * hh);
+      st.qf[kc] = *(const u32x4*)(qg + (long long)myq * D + 16 * kc + 8 * x.hh);
     else
-      qf[kc] = u32x4{0u, 0u, 0u, 0u};
+      st.qf[kc] = u32x4{0u, 0u, 0u, 0u};
   }
-
-  f32x16 oacc[S::kOutTiles];
 #pragma unroll
-  for (int ct = 0; ct < S::kOutTiles; ++ct) oacc[ct] = f32x16{};
-  float m_run = -INFINITY;  // running max of scale*log2(e)*score
-  float l_run = 0.f;        // running sum of exp2(... - m_run) over this half-wave's keys
-  const float c = p.scale_log2;
+  for (int ct = 0; ct < S::kOutTiles; ++ct) st.oacc[ct] = f32x16{};
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
 
-  // Global -> register staging of one K/V tile (zero rows past the end).
-  u32x4 kreg[S::kChunksPerThread], vreg[S::kChunksPerThread];
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int u = 0; u < S::kChunksPerThread; ++u) {
-      const int ci = tid + u * kThreads;
-      const int row = ci / S::kChunks;
-      const int ch = ci % S::kChunks;
-      const int key = t * kBC + row;
-      if (key < N) {
-        kreg[u] = *(const u32x4*)(kg + (long long)key * D + ch * 8);
-        vreg[u] = *(const u32x4*)(vg + (long long)key * D + ch * 8);
-      } else {
-        kreg[u] = u32x4{0u, 0u, 0u, 0u};
-        vreg[u] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int u = 0; u < S::kChunksPerThread; ++u) {
-      const int ci = tid + u * kThreads;
-      const int row = ci / S::kChunks;
-      const int ch = ci % S::kChunks;
-      *(u32x4*)(sK + k_off<D>(row, ch)) = kreg[u];
-      *(u32x4*)(sV + v_off<D>(row, ch * 8)) = vreg[u];
-    }
-  };
-
-  // Lane geometry of the transposing V read (see the header comment).
-  const int g16 = lane >> 4;
-  const int gi = lane & 15;
-  const int v_row_lane = 4 * hh + (gi >> 2);
-  const int v_col_lane = 16 * (g16 & 1) + 4 * (gi & 3);
-
-  if (t_beg < t_end) load_tile(t_beg);
-  for (int t = t_beg; t < t_end; ++t) {
-    __syncthreads();  // every wavefront is done with the previous tile
-    store_tile();
+  // Tiles alternate between the two buffers.  Before each tile: this wave's
+  // copies have landed; after the barrier everyone's have, and every wave is
+  // done reading the buffer the next copies go to.
+  for (int t = t_beg; t < x.t_end; t += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < t_end) load_tile(t + 1);  // in flight while this tile computes
-
-    const int kb = t * kBC;
-    const int ke = kb + kBC - 1;
-    const bool skip = (wq0 >= N) || (causal && kb > wq1) || (wl >= 0 && ke < wq0 - wl);
-    if (skip) continue;
-    const bool need_mask = (ke >= N) || (causal && ke > wq0) || (wl >= 0 && kb < wq1 - wl);
-
-    // ---- scores: S^T = K Q^T, keys kb..kb+31 in s0 and kb+32..kb+63 in s1
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
-#pragma unroll
-    for (int kc = 0; kc < S::kSteps; ++kc) {
-      const u32x4 a0 = *(const u32x4*)(sK + k_off<D>(l32, 2 * kc + hh));
-      const u32x4 a1 = *(const u32x4*)(sK + k_off<D>(32 + l32, 2 * kc + hh));
-      s0 = E::mma(a0, qf[kc], s0);
-      s1 = E::mma(a1, qf[kc], s1);
-    }
-
-    // ---- mask: only on tiles that cross the causal diagonal, the window
-    // edge or the end of the sequence
-    if (need_mask) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb + 8 * (i >> 2) + 4 * hh + (i & 3);
-        const bool h0 = key >= N || (causal && key > myq) || (wl >= 0 && key < myq - wl);
-        const bool h1 = key + 32 >= N || (causal && key + 32 > myq) || (wl >= 0 && key + 32 < myq - wl);
-        s0[i] = h0 ? -INFINITY : s0[i];
-        s1[i] = h1 ? -INFINITY : s1[i];
-      }
-    }
-
-    // ---- online softmax (base 2, scale folded into the exponent)
-    float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-    float mlo, mhi;
-    half_pair(mx, mlo, mhi);
-    mx = fmaxf(mlo, mhi);
-    const float m_new = fmaxf(m_run, mx * c);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // nothing visible yet
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    float rs = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, -m_use));
-      s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -m_use));
-      rs += s0[i] + s1[i];
-    }
-    l_run = l_run * alpha + rs;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-      for (int ct = 0; ct < S::kOutTiles; ++ct) oacc[ct] *= alpha;
-    }
-
-    // ---- P^T operands: the lane's own probabilities, 8 keys per k-step
-    u32x4 pf[4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      pf[j] = u32x4{E::pack2(s0[8 * j + 0], s0[8 * j + 1]), E::pack2(s0[8 * j + 2], s0[8 * j + 3]),
-                    E::pack2(s0[8 * j + 4], s0[8 * j + 5]), E::pack2(s0[8 * j + 6], s0[8 * j + 7])};
-      pf[2 + j] = u32x4{E::pack2(s1[8 * j + 0], s1[8 * j + 1]), E::pack2(s1[8 * j + 2], s1[8 * j + 3]),
-                        E::pack2(s1[8 * j + 4], s1[8 * j + 5]), E::pack2(s1[8 * j + 6], s1[8 * j + 7])};
-    }
-
-    // ---- O^T += V^T P^T.  k-step mc covers keys 16mc..16mc+15 in the order
-    // the accumulator hands them over: half-wave hh holds keys
-    // 16mc + 4hh + {0..3} and 16mc + 8 + 4hh + {0..3}.
-#pragma unroll
-    for (int ct = 0; ct < S::kOutTiles; ++ct) {
-      const int col = 32 * ct + v_col_lane;
-#pragma unroll
-      for (int mc = 0; mc < 4; ++mc) {
-        const int ra = 16 * mc + v_row_lane;
-        const s16x4 lo = lds_read_tr(sV, v_off<D>(ra, col));
-        const s16x4 hi = lds_read_tr(sV, v_off<D>(ra + 8, col));
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-        const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 a = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-        oacc[ct] = E::mma(a, pf[mc], oacc[ct]);
-      }
+    tile_step<E, D>(sK0, sV0, sK1, sV1, x, st, t);
+    if (t + 1 < x.t_end) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      tile_step<E, D>(sK1, sV1, sK0, sV0, x, st, t + 1);
     }
   }
 
   // ---- epilogue: one division per row, store O and the logsumexp
   float llo, lhi;
-  half_pair(l_run, llo, lhi);
+  half_pair(st.l_run, llo, lhi);
   const float l_tot = llo + lhi;
   if (myq < N) {
     const float inv = 1.f / l_tot;
@@ -313,13 +378,13 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_mfma_kernel(FwdParams p) {
     for (int ct = 0; ct < S::kOutTiles; ++ct) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const u32x2 w = u32x2{E::pack2(oacc[ct][4 * gq + 0] * inv, oacc[ct][4 * gq + 1] * inv),
-                              E::pack2(oacc[ct][4 * gq + 2] * inv, oacc[ct][4 * gq + 3] * inv)};
-        *(u32x2*)(og + 32 * ct + 8 * gq + 4 * hh) = w;
+        const u32x2 w = u32x2{E::pack2(st.oacc[ct][4 * gq + 0] * inv, st.oacc[ct][4 * gq + 1] * inv),
+                              E::pack2(st.oacc[ct][4 * gq + 2] * inv, st.oacc[ct][4 * gq + 3] * inv)};
+        *(u32x2*)(og + 32 * ct + 8 * gq + 4 * x.hh) = w;
       }
     }
-    if (hh == 0 && p.lse != nullptr)
-      p.lse[(long long)it.bh * N + myq] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    if (x.hh == 0 && p.lse != nullptr)
+      p.lse[(long long)it.bh * N + myq] = (st.m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
 }
 
