@@ -141,35 +141,56 @@ __device__ __forceinline__ s16x4 lds_read_tr(const unsigned short* base, int off
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
 }
 
-// Start the copy of key tile [kb, kb + kBC) of K and V from device memory
-// straight into LDS (buffer loads with the LDS destination; no registers).
-// Each wave moves kLoadsPerWave 1-KiB pieces of each tensor: lane l fills LDS
-// bytes 16l..16l+15 of its piece, so it fetches the logical chunk that the
-// swizzle maps there.  Rows past the end of the sequence are outside the
-// buffer's range and arrive as zeros.
+// Per-lane byte offsets (within one tile) of this lane's pieces of the
+// direct-to-LDS copies.  Each wave moves kLoadsPerWave 1-KiB pieces of each
+// tensor per tile: lane l fills LDS bytes 16l..16l+15 of its piece, so it
+// fetches the logical chunk that the swizzle maps there.
 template <int D>
-__device__ __forceinline__ void load_tile_async(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                                unsigned short* sk, unsigned short* sv, int kb,
-                                                int wave, int lane) {
+struct LoadOffsets {
+  int k[Shape<D>::kLoadsPerWave];
+  int v[Shape<D>::kLoadsPerWave];
+  __device__ __forceinline__ void init(int wave, int lane) {
+    using S = Shape<D>;
+#pragma unroll
+    for (int u = 0; u < S::kLoadsPerWave; ++u) {
+      const int piece = wave * S::kLoadsPerWave + u;
+      const int row = piece * S::kRowsPerLoad + lane / S::kChunks;
+      const int pch = lane % S::kChunks;  // physical chunk this lane fills
+      k[u] = row * S::kRowBytes + ((pch ^ k_swz<D>(row)) << 4);
+      v[u] = row * S::kRowBytes + ((pch ^ v_swz<D>(row)) << 4);
+    }
+  }
+};
+
+// Start copying key tile t of K (or V) from device memory straight into LDS
+// (buffer loads with the LDS destination; no registers).  The tile's start
+// is a wave-uniform byte offset.  Rows past the end of the sequence lie
+// outside the buffer's range and arrive as zeros.
+template <int D>
+__device__ __forceinline__ void copy_tile_async(__amdgpu_buffer_rsrc_t r, const int* lane_off,
+                                                unsigned short* dst, int t, int wave) {
   using S = Shape<D>;
+  const int tile_bytes = t * (kBC * S::kRowBytes);
 #pragma unroll
   for (int u = 0; u < S::kLoadsPerWave; ++u) {
     const int piece = wave * S::kLoadsPerWave + u;
-    const int row = piece * S::kRowsPerLoad + lane / S::kChunks;
-    const int pch = lane % S::kChunks;  // physical chunk this lane fills
-    const int gk = (kb + row) * S::kRowBytes + ((pch ^ k_swz<D>(row)) << 4);
-    const int gv = (kb + row) * S::kRowBytes + ((pch ^ v_swz<D>(row)) << 4);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(sk + piece * 512), 16, gk, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(sv + piece * 512), 16, gv, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + piece * 512), 16, lane_off[u],
+                                             tile_bytes, 0, 0);
   }
 }
 
 constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 
+// A row's running max may lag the true max by up to this much (log2 units)
+// before the partial output is rescaled; probabilities then stay <= 2^8.
+constexpr float kRescaleSlack = 8.0f;
+
 // Per-lane constants of one workgroup's key loop.
+template <int D>
 struct LoopCtx {
   __amdgpu_buffer_rsrc_t rk, rv;  // this (batch, kv head)'s K and V, bounded to N rows
-  int N, wl, t_end;
+  LoadOffsets<D> off;
+  int N, wl, t_beg, t_end;
   int wave, lane, l32, hh;
   int wq0, wq1;                   // first and last valid row of the wavefront
   int vis_lo;                     // first visible key of this lane's row
@@ -184,77 +205,74 @@ template <int D>
 struct RowState {
   u32x4 qf[Shape<D>::kSteps];         // q row as the B operand
   f32x16 oacc[Shape<D>::kOutTiles];   // unnormalised O^T columns
-  float m_run;                        // running max of scale*log2(e)*score
-  float l_run;                        // running sum of exp2(. - m_run), this half-wave's keys
+  float m_use;                        // max used in the exponents (scale*log2(e) units)
+  float l_run;                        // running sum of exp2(. - m_use), this half-wave's keys
 };
 
-// One key tile: start the copy of tile t+1 into the other buffers, then
-// fold tile t (already in cK/cV) into the row state.  The buffer pointers
-// are restrict-qualified: the copies into nK/nV never touch cK/cV, which lets
-// the LDS reads below proceed while those copies are in flight.
+// Scores of key tile t: S^T = K Q^T, keys 64t..64t+31 in s0, +32..+63 in s1.
 template <typename E, int D>
-__device__ __forceinline__ void tile_step(const unsigned short* __restrict__ cK,
-                                          const unsigned short* __restrict__ cV,
-                                          unsigned short* __restrict__ nK,
-                                          unsigned short* __restrict__ nV, const LoopCtx& x,
-                                          RowState<D>& st, int t) {
-  using S = Shape<D>;
-  if (t + 1 < x.t_end) load_tile_async<D>(x.rk, x.rv, nK, nV, (t + 1) * kBC, x.wave, x.lane);
-
-  const int kb = t * kBC;
-  const int ke = kb + kBC - 1;
-  const bool skip = (x.wq0 >= x.N) || (x.causal && kb > x.wq1) || (x.wl >= 0 && ke < x.wq0 - x.wl);
-  if (skip) return;
-  const bool need_mask = (ke >= x.N) || (x.causal && ke > x.wq0) || (x.wl >= 0 && kb < x.wq1 - x.wl);
-
-  // ---- scores: S^T = K Q^T, keys kb..kb+31 in s0 and kb+32..kb+63 in s1
-  f32x16 s0 = f32x16{}, s1 = f32x16{};
+__device__ __forceinline__ void tile_scores(const unsigned short* __restrict__ cK, const LoopCtx<D>& x,
+                                            const RowState<D>& st, f32x16& s0, f32x16& s1) {
+  s0 = f32x16{};
+  s1 = f32x16{};
 #pragma unroll
-  for (int kc = 0; kc < S::kSteps; ++kc) {
+  for (int kc = 0; kc < Shape<D>::kSteps; ++kc) {
     const u32x4 a0 = *(const u32x4*)(cK + k_off<D>(x.l32, 2 * kc + x.hh));
     const u32x4 a1 = *(const u32x4*)(cK + k_off<D>(32 + x.l32, 2 * kc + x.hh));
     s0 = E::mma(a0, st.qf[kc], s0);
     s1 = E::mma(a1, st.qf[kc], s1);
   }
+}
 
-  // ---- mask (tiles crossing the diagonal, the window edge or the end):
-  // key kb + off is visible iff 0 <= kb + off - vis_lo <= vis_span
-  if (need_mask) {
-    const int base = kb - x.vis_lo + 4 * x.hh;
+// Mask tile t when it crosses the causal diagonal, the window edge or the
+// sequence end for some row of the wavefront: key kb + off is visible iff
+// 0 <= kb + off - vis_lo <= vis_span.
+template <int D>
+__device__ __forceinline__ void tile_mask(const LoopCtx<D>& x, int t, f32x16& s0, f32x16& s1) {
+  const int kb = t * kBC;
+  const int ke = kb + kBC - 1;
+  const bool need_mask = (ke >= x.N) || (x.causal && ke > x.wq0) || (x.wl >= 0 && kb < x.wq1 - x.wl);
+  if (!need_mask) return;
+  const int base = kb - x.vis_lo + 4 * x.hh;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int off = 8 * (i >> 2) + (i & 3);
-      s0[i] = ((unsigned)(base + off) <= x.vis_span) ? s0[i] : -INFINITY;
-      s1[i] = ((unsigned)(base + off + 32) <= x.vis_span) ? s1[i] : -INFINITY;
-    }
+  for (int i = 0; i < 16; ++i) {
+    const int off = 8 * (i >> 2) + (i & 3);
+    s0[i] = ((unsigned)(base + off) <= x.vis_span) ? s0[i] : -INFINITY;
+    s1[i] = ((unsigned)(base + off + 32) <= x.vis_span) ? s1[i] : -INFINITY;
   }
+}
 
-  // ---- online softmax (base 2, scale folded into the exponent)
+// Online softmax of one score tile (base 2, scale folded into the
+// exponent): turns s0/s1 into the P^T operands pf, updates the row's
+// reference max and sum, and returns the factor the partial output must be
+// multiplied by (1 unless the reference max moved).
+template <typename E, int D>
+__device__ __forceinline__ float tile_softmax(const LoopCtx<D>& x, RowState<D>& st, f32x16& s0, f32x16& s1,
+                                              u32x4* pf) {
   float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
   for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
   float mlo, mhi;
   half_pair(mx, mlo, mhi);
-  mx = fmaxf(mlo, mhi);
-  const float m_new = fmaxf(st.m_run, mx * x.c);
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // nothing visible yet
-  const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_use);
-  st.m_run = m_new;
+  mx = fmaxf(mlo, mhi) * x.c;
+  // move the row's reference max only when the true max got ahead of it by
+  // more than the slack (always on the first visible key)
+  // (no NaN can arise: when bumped, mx is finite and m_use - mx is finite
+  // or -inf; otherwise the factor is exactly 1)
+  const bool bump = mx > st.m_use + kRescaleSlack;
+  const float alpha = bump ? __builtin_amdgcn_exp2f(st.m_use - mx) : 1.f;
+  const float m_new = bump ? mx : st.m_use;
+  st.m_use = m_new;
+  const float m_exp = (m_new == -INFINITY) ? 0.f : m_new;        // nothing visible yet
   float rs = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], x.c, -m_use));
-    s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], x.c, -m_use));
+    s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], x.c, -m_exp));
+    s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], x.c, -m_exp));
     rs += s0[i] + s1[i];
   }
-  st.l_run = st.l_run * alpha + rs;
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-    for (int ct = 0; ct < S::kOutTiles; ++ct) st.oacc[ct] *= alpha;
-  }
-
-  // ---- P^T operands: the lane's own probabilities, 8 keys per k-step
-  u32x4 pf[4];
+  st.l_run = __builtin_fmaf(st.l_run, alpha, rs);
+  // P^T operands: the lane's own probabilities, 8 keys per k-step
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     pf[j] = u32x4{E::pack2(s0[8 * j + 0], s0[8 * j + 1]), E::pack2(s0[8 * j + 2], s0[8 * j + 3]),
@@ -262,18 +280,23 @@ __device__ __forceinline__ void tile_step(const unsigned short* __restrict__ cK,
     pf[2 + j] = u32x4{E::pack2(s1[8 * j + 0], s1[8 * j + 1]), E::pack2(s1[8 * j + 2], s1[8 * j + 3]),
                       E::pack2(s1[8 * j + 4], s1[8 * j + 5]), E::pack2(s1[8 * j + 6], s1[8 * j + 7])};
   }
+  return alpha;
+}
 
-  // ---- O^T += V^T P^T.  k-step mc covers keys 16mc..16mc+15 in the order
-  // the accumulator hands them over: half-wave hh holds keys
-  // 16mc + 4hh + {0..3} and 16mc + 8 + 4hh + {0..3}.
+// O^T += V^T P^T for one tile.  k-step mc covers keys 16mc..16mc+15 in the
+// order the score accumulator hands them over: half-wave hh holds keys
+// 16mc + 4hh + {0..3} and 16mc + 8 + 4hh + {0..3}.
+template <typename E, int D>
+__device__ __forceinline__ void tile_pv(const unsigned short* __restrict__ vC, const LoopCtx<D>& x,
+                                        RowState<D>& st, const u32x4* pf) {
 #pragma unroll
-  for (int ct = 0; ct < S::kOutTiles; ++ct) {
+  for (int ct = 0; ct < Shape<D>::kOutTiles; ++ct) {
     const int col = 32 * ct + x.v_col_lane;
 #pragma unroll
     for (int mc = 0; mc < 4; ++mc) {
       const int ra = 16 * mc + x.v_row_lane;
-      const s16x4 lo = lds_read_tr(cV, v_off<D>(ra, col));
-      const s16x4 hi = lds_read_tr(cV, v_off<D>(ra + 8, col));
+      const s16x4 lo = lds_read_tr(vC, v_off<D>(ra, col));
+      const s16x4 hi = lds_read_tr(vC, v_off<D>(ra + 8, col));
       const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
       const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
       const u32x4 a = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
@@ -282,21 +305,85 @@ __device__ __forceinline__ void tile_step(const unsigned short* __restrict__ cK,
   }
 }
 
+__device__ __forceinline__ void rescale_if_needed(float alpha, f32x16* oacc, int tiles) {
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+    for (int ct = 0; ct < tiles; ++ct) oacc[ct] *= alpha;
+  }
+}
+
+// One step of the key loop, software-pipelined so that the vector units'
+// softmax of tile t runs while the matrix cores accumulate P(t-1) V(t-1):
+//   1. S(t) = K(t) Q^T on the matrix cores; meanwhile the vector units bring
+//      O to the reference max that P(t-1) was computed with (the factor
+//      from tile t-1's softmax; 1 unless that max moved);
+//   2. softmax(S(t)) -> P(t), interleaved with O += P(t-1) V(t-1).
+// K(t) and V(t-1) are in LDS when the step starts; it starts the copies of
+// K(t+1) into kN and V(t) into vN.  The buffer pointers are restrict-
+// qualified: copies into kN/vN never touch kC/vC, which lets the LDS reads
+// proceed while those copies are in flight.
+template <typename E, int D, bool kHasPrev>
+__device__ __forceinline__ void pipeline_step(const unsigned short* __restrict__ kC,  // holds K(t)
+                                              unsigned short* __restrict__ kN,        // gets K(t+1)
+                                              const unsigned short* __restrict__ vC,  // holds V(t-1)
+                                              unsigned short* __restrict__ vN,        // gets V(t)
+                                              const LoopCtx<D>& x, RowState<D>& st, u32x4* pf_prev,
+                                              float& alpha_prev, int t) {
+  using S = Shape<D>;
+  if (t + 1 < x.t_end) copy_tile_async<D>(x.rk, x.off.k, kN, t + 1, x.wave);
+  copy_tile_async<D>(x.rv, x.off.v, vN, t, x.wave);
+
+  f32x16 s0, s1;
+  tile_scores<E, D>(kC, x, st, s0, s1);
+  tile_mask<D>(x, t, s0, s1);
+
+  // P(t-1) was computed with the reference max as it stood after tile t-1;
+  // O still carries the scale before it: bring O to that scale first.
+  if (kHasPrev) rescale_if_needed(alpha_prev, st.oacc, S::kOutTiles);
+
+  u32x4 pf[4];
+  const float alpha = tile_softmax<E, D>(x, st, s0, s1, pf);
+  if (kHasPrev) {
+    tile_pv<E, D>(vC, x, st, pf_prev);
+    // interleave: each PV MFMA follows a slice of the softmax work, and its
+    // two transposing reads were issued two MFMAs earlier
+    constexpr int kPv = 4 * S::kOutTiles;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS read
+#pragma unroll
+    for (int g = 0; g < kPv; ++g) {
+      if (g + 2 < kPv) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);                    // VALU
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pf_prev[j] = pf[j];
+  alpha_prev = alpha;
+}
+
+// Wait for this wave's copies, then for every wave's: the copies started in
+// the previous step have landed and every wave is done with the buffers the
+// next copies will overwrite.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 template <typename E, int D>
 __global__ void __launch_bounds__(kThreads, 2) fwd_mfma_kernel(FwdParams p) {
   using S = Shape<D>;
-  // two K/V buffers as separate objects
+  // two K and two V buffers, as separate objects
   __shared__ __attribute__((aligned(16))) unsigned short sK0[kBC * D];
-  __shared__ __attribute__((aligned(16))) unsigned short sV0[kBC * D];
   __shared__ __attribute__((aligned(16))) unsigned short sK1[kBC * D];
+  __shared__ __attribute__((aligned(16))) unsigned short sV0[kBC * D];
   __shared__ __attribute__((aligned(16))) unsigned short sV1[kBC * D];
 
-  LoopCtx x;
+  LoopCtx<D> x;
   const int tid = threadIdx.x;
   x.lane = tid & (kWaveSize - 1);
   x.wave = tid / kWaveSize;
   x.l32 = x.lane & 31;
   x.hh = x.lane >> 5;
+  x.off.init(x.wave, x.lane);
 
   const WorkItem it = decode_work_item(p, blockIdx.x);
   const int N = p.N;
@@ -325,7 +412,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_mfma_kernel(FwdParams p) {
   // starts window_left keys before its first row.
   const int kend = x.causal ? min(N, q0 + kBR) : N;
   const int kbeg = x.wl >= 0 ? max(0, q0 - x.wl) : 0;
-  const int t_beg = kbeg / kBC;
+  x.t_beg = kbeg / kBC;
   x.t_end = (kend + kBC - 1) / kBC;
 
   // Visible keys of this lane's row form one range [vis_lo, vis_lo + vis_span].
@@ -338,8 +425,6 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_mfma_kernel(FwdParams p) {
   x.v_row_lane = 4 * x.hh + (gi >> 2);
   x.v_col_lane = 16 * (g16 & 1) + 4 * (gi & 3);
 
-  if (t_beg < x.t_end) load_tile_async<D>(x.rk, x.rv, sK0, sV0, t_beg * kBC, x.wave, x.lane);
-
   RowState<D> st;
 #pragma unroll
   for (int kc = 0; kc < S::kSteps; ++kc) {
@@ -350,22 +435,32 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_mfma_kernel(FwdParams p) {
   }
 #pragma unroll
   for (int ct = 0; ct < S::kOutTiles; ++ct) st.oacc[ct] = f32x16{};
-  st.m_run = -INFINITY;
+  st.m_use = -INFINITY;
   st.l_run = 0.f;
 
-  // Tiles alternate between the two buffers.  Before each tile: this wave's
-  // copies have landed; after the barrier everyone's have, and every wave is
-  // done reading the buffer the next copies go to.
-  for (int t = t_beg; t < x.t_end; t += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    tile_step<E, D>(sK0, sV0, sK1, sV1, x, st, t);
+  // Buffers alternate with the tile index relative to t_beg: K(t) and V(t)
+  // live in buffer (t - t_beg) % 2.
+  const int t0 = x.t_beg;
+  copy_tile_async<D>(x.rk, x.off.k, sK0, t0, x.wave);
+  u32x4 pf_prev[4];
+  float alpha_prev = 1.f;
+  tile_barrier();
+  pipeline_step<E, D, false>(sK0, sK1, sV1, sV0, x, st, pf_prev, alpha_prev, t0);
+  for (int t = t0 + 1; t < x.t_end; t += 2) {
+    tile_barrier();
+    pipeline_step<E, D, true>(sK1, sK0, sV0, sV1, x, st, pf_prev, alpha_prev, t);
     if (t + 1 < x.t_end) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      tile_step<E, D>(sK1, sV1, sK0, sV0, x, st, t + 1);
+      tile_barrier();
+      pipeline_step<E, D, true>(sK0, sK1, sV1, sV0, x, st, pf_prev, alpha_prev, t + 1);
     }
   }
+  // drain: P(t_end-1) V(t_end-1)
+  tile_barrier();
+  rescale_if_needed(alpha_prev, st.oacc, S::kOutTiles);
+  if (((x.t_end - 1 - t0) & 1) == 0)
+    tile_pv<E, D>(sV0, x, st, pf_prev);
+  else
+    tile_pv<E, D>(sV1, x, st, pf_prev);
 
   // ---- epilogue: one division per row, store O and the logsumexp
   float llo, lhi;
@@ -384,7 +479,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_mfma_kernel(FwdParams p) {
       }
     }
     if (x.hh == 0 && p.lse != nullptr)
-      p.lse[(long long)it.bh * N + myq] = (st.m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      p.lse[(long long)it.bh * N + myq] = (st.m_use + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
 }
 
