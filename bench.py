@@ -167,8 +167,12 @@ def run(args, name, with_cpu):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The GPU needs ~30 ms of sustained work to leave its low-clock state
+    # (per-launch time settles after ~50 launches of the causal 8k workload),
+    # so the default warmup covers that and the timed steps measure the
+    # steady state.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="causal_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="one line per workload (no CPU baseline)")

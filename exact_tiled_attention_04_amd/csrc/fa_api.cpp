@@ -69,6 +69,10 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
         overlap(lse, n_l, v, n_kv))
       return fail(FA_ERR_INVALID_ARG, "lse overlaps o or an input");
   }
+  // K/V tiles are addressed with 32-bit byte offsets within one head
+  // (a few tiles of slack past the end)
+  if ((uint64_t)N * d * elem_size(dtype) + (1u << 20) > (uint64_t)INT32_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "N=%d too long for d=%d (one head must stay below 2 GiB)", N, d);
   const long long rows = dtype == FA_DTYPE_F32 ? fa::f32_rows_per_workgroup() : fa::mfma_rows_per_workgroup();
   const long long items = (long long)B * Hq * ((N + rows - 1) / rows);
   if (items > fa::kMaxGridItems)

@@ -313,27 +313,32 @@ __device__ __forceinline__ void rescale_if_needed(float alpha, f32x16* oacc, int
 
 // One step of the key loop, software-pipelined so that the vector units'
 // softmax of tile t runs while the matrix cores accumulate P(t-1) V(t-1):
-//   1. S(t) = K(t) Q^T on the matrix cores; meanwhile the vector units bring
-//      O to the reference max that P(t-1) was computed with (the factor
-//      from tile t-1's softmax; 1 unless that max moved);
-//   2. softmax(S(t)) -> P(t), interleaved with O += P(t-1) V(t-1).
-// K(t) and V(t-1) are in LDS when the step starts; it starts the copies of
-// K(t+1) into kN and V(t) into vN.  The buffer pointers are restrict-
-// qualified: copies into kN/vN never touch kC/vC, which lets the LDS reads
-// proceed while those copies are in flight.
+//   1. S(t) = K(t) Q^T on the matrix cores, at raised wave priority: while
+//      this wave issues its score MFMAs, the other wave on the SIMD (from the
+//      other workgroup) fills the vector units with its softmax;
+//   2. softmax(S(t)) -> P(t), interleaved with O += P(t-1) V(t-1), after O is
+//      brought to the reference max that P(t-1) was computed with.
+// K(t) and V(t-1) are in LDS when the step starts.  The step first starts
+// copying V(t) into vN (V(t-2)'s buffer), then K(t+2) into kN (K(t-1)'s);
+// both buffers were last read in step t-1.  K thus travels two steps ahead,
+// V one.  The buffer pointers are restrict-qualified: copy targets are never
+// read in this step, which lets the LDS reads proceed while copies are in
+// flight.
 template <typename E, int D, bool kHasPrev>
 __device__ __forceinline__ void pipeline_step(const unsigned short* __restrict__ kC,  // holds K(t)
-                                              unsigned short* __restrict__ kN,        // gets K(t+1)
+                                              unsigned short* __restrict__ kN,        // gets K(t+2)
                                               const unsigned short* __restrict__ vC,  // holds V(t-1)
                                               unsigned short* __restrict__ vN,        // gets V(t)
                                               const LoopCtx<D>& x, RowState<D>& st, u32x4* pf_prev,
                                               float& alpha_prev, int t) {
   using S = Shape<D>;
-  if (t + 1 < x.t_end) copy_tile_async<D>(x.rk, x.off.k, kN, t + 1, x.wave);
   copy_tile_async<D>(x.rv, x.off.v, vN, t, x.wave);
+  copy_tile_async<D>(x.rk, x.off.k, kN, t + 2, x.wave);  // past the end: zeros, never read
 
   f32x16 s0, s1;
+  __builtin_amdgcn_s_setprio(2);
   tile_scores<E, D>(kC, x, st, s0, s1);
+  __builtin_amdgcn_s_setprio(0);
   tile_mask<D>(x, t, s0, s1);
 
   // P(t-1) was computed with the reference max as it stood after tile t-1;
@@ -360,27 +365,32 @@ __device__ __forceinline__ void pipeline_step(const unsigned short* __restrict__
   alpha_prev = alpha;
 }
 
-// Wait for this wave's copies, then for every wave's: the copies started in
-// the previous step have landed and every wave is done with the buffers the
-// next copies will overwrite.
+// Wait until at most this wave's newest kInFlight copies are outstanding,
+// then for every wave to do so: the copies the next step reads have landed
+// and every wave is done with the buffers the next copies will overwrite.
+// (A plain workgroup barrier would also wait for every outstanding copy; the
+// memory clobber keeps the compiler from moving memory operations across.)
+template <int kInFlight>
 __device__ __forceinline__ void tile_barrier() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  static_assert(kInFlight >= 0 && kInFlight < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kInFlight) : "memory");
 }
 
 template <typename E, int D>
 __global__ void __launch_bounds__(kThreads, 2) fwd_mfma_kernel(FwdParams p) {
   using S = Shape<D>;
-  // two K and two V buffers, as separate objects
+  // three K and two V buffers, as separate objects (80 KiB at d = 128, so two
+  // workgroups share a compute unit)
   __shared__ __attribute__((aligned(16))) unsigned short sK0[kBC * D];
   __shared__ __attribute__((aligned(16))) unsigned short sK1[kBC * D];
+  __shared__ __attribute__((aligned(16))) unsigned short sK2[kBC * D];
   __shared__ __attribute__((aligned(16))) unsigned short sV0[kBC * D];
   __shared__ __attribute__((aligned(16))) unsigned short sV1[kBC * D];
 
   LoopCtx<D> x;
   const int tid = threadIdx.x;
   x.lane = tid & (kWaveSize - 1);
-  x.wave = tid / kWaveSize;
+  x.wave = __builtin_amdgcn_readfirstlane(tid / kWaveSize);  // wave-uniform: keep it scalar
   x.l32 = x.lane & 31;
   x.hh = x.lane >> 5;
   x.off.init(x.wave, x.lane);
@@ -438,24 +448,36 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_mfma_kernel(FwdParams p) {
   st.m_use = -INFINITY;
   st.l_run = 0.f;
 
-  // Buffers alternate with the tile index relative to t_beg: K(t) and V(t)
-  // live in buffer (t - t_beg) % 2.
+  // With i = t - t_beg: K(t) lives in K buffer i % 3, V(t) in V buffer i % 2.
+  // The step loop is unrolled six ways so every buffer choice is a
+  // compile-time constant (LDS addresses fold into instruction offsets).
+  auto kbuf = [&](int j) { return j == 0 ? sK0 : (j == 1 ? sK1 : sK2); };
+  auto vbuf = [&](int j) { return j == 0 ? sV0 : sV1; };
+  constexpr int kCopyLoads = S::kLoadsPerWave;  // loads per copy per wave
   const int t0 = x.t_beg;
   copy_tile_async<D>(x.rk, x.off.k, sK0, t0, x.wave);
+  copy_tile_async<D>(x.rk, x.off.k, sK1, t0 + 1, x.wave);  // past the end: zeros, never read
   u32x4 pf_prev[4];
   float alpha_prev = 1.f;
-  tile_barrier();
-  pipeline_step<E, D, false>(sK0, sK1, sV1, sV0, x, st, pf_prev, alpha_prev, t0);
-  for (int t = t0 + 1; t < x.t_end; t += 2) {
-    tile_barrier();
-    pipeline_step<E, D, true>(sK1, sK0, sV0, sV1, x, st, pf_prev, alpha_prev, t);
-    if (t + 1 < x.t_end) {
-      tile_barrier();
-      pipeline_step<E, D, true>(sK0, sK1, sV1, sV0, x, st, pf_prev, alpha_prev, t + 1);
-    }
+  tile_barrier<0>();
+  pipeline_step<E, D, false>(sK0, sK2, sV1, sV0, x, st, pf_prev, alpha_prev, t0);
+  auto step = [&](auto uc, int t) {
+    constexpr int u = decltype(uc)::value;  // (t - t0) % 6
+    // everything but the previous step's K copy (its last) has landed
+    tile_barrier<kCopyLoads>();
+    pipeline_step<E, D, true>(kbuf(u % 3), kbuf((u + 2) % 3), vbuf((u + 1) % 2), vbuf(u % 2), x, st,
+                              pf_prev, alpha_prev, t);
+  };
+  for (int t = t0 + 1; t < x.t_end; t += 6) {
+    step(std::integral_constant<int, 1>{}, t);
+    if (t + 1 < x.t_end) step(std::integral_constant<int, 2>{}, t + 1);
+    if (t + 2 < x.t_end) step(std::integral_constant<int, 3>{}, t + 2);
+    if (t + 3 < x.t_end) step(std::integral_constant<int, 4>{}, t + 3);
+    if (t + 4 < x.t_end) step(std::integral_constant<int, 5>{}, t + 4);
+    if (t + 5 < x.t_end) step(std::integral_constant<int, 0>{}, t + 5);
   }
   // drain: P(t_end-1) V(t_end-1)
-  tile_barrier();
+  tile_barrier<kCopyLoads>();
   rescale_if_needed(alpha_prev, st.oacc, S::kOutTiles);
   if (((x.t_end - 1 - t0) & 1) == 0)
     tile_pv<E, D>(sV0, x, st, pf_prev);

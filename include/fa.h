@@ -63,7 +63,7 @@ typedef enum {
   FA_ERR_INVALID_ARG = -1, /* null pointer, negative size, Hq % Hkv != 0,
                               window_left < -1, non-finite scale          */
   FA_ERR_UNSUPPORTED = -2, /* d not 64 or 128, unknown dtype, scale <= 0,
-                              a size whose offsets overflow 64 bits       */
+                              one head's K or V of 2 GiB or more          */
   FA_ERR_MISALIGNED = -3,  /* q, k, v or o not 16-byte aligned, lse not
                               4-byte aligned                              */
   FA_ERR_HIP = -4          /* the HIP runtime reported an error at launch */
