@@ -61,7 +61,22 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaveSize * kWaves;
 constexpr int kRowsPerWave = 32;
 constexpr int kBR = kWaves * kRowsPerWave;  // query rows per workgroup
-constexpr int kBC = 64;                     // keys per K/V tile
+#ifndef FA_KEYS_PER_TILE
+#define FA_KEYS_PER_TILE 64
+#endif
+#ifndef FA_V_BUFFERS
+#define FA_V_BUFFERS 2
+#endif
+#ifndef FA_WAVES_PER_SIMD
+#define FA_WAVES_PER_SIMD 2
+#endif
+constexpr int kBC = FA_KEYS_PER_TILE;       // keys per K/V tile (32 or 64)
+constexpr int kHalves = kBC / 32;           // 32-key score blocks per tile
+constexpr int kKBufs = 3;                   // LDS buffers for K (K travels two tiles ahead)
+constexpr int kVBufs = FA_V_BUFFERS;        // 2: V one tile ahead; 3: two tiles ahead
+constexpr int kWavesPerSimd = FA_WAVES_PER_SIMD;
+static_assert(kBC == 32 || kBC == 64, "tile width");
+static_assert(kVBufs == 2 || kVBufs == 3, "V buffering");
 constexpr float kLn2 = 0.69314718055994531f;
 
 struct Bf16 {
@@ -209,18 +224,19 @@ struct RowState {
   float l_run;                        // running sum of exp2(. - m_use), this half-wave's keys
 };
 
-// Scores of key tile t: S^T = K Q^T, keys 64t..64t+31 in s0, +32..+63 in s1.
+// Scores of key tile t: S^T = K Q^T; s[h] holds keys kBC*t + 32h .. +31.
 template <typename E, int D>
 __device__ __forceinline__ void tile_scores(const unsigned short* __restrict__ cK, const LoopCtx<D>& x,
-                                            const RowState<D>& st, f32x16& s0, f32x16& s1) {
-  s0 = f32x16{};
-  s1 = f32x16{};
+                                            const RowState<D>& st, f32x16 (&s)[kHalves]) {
+#pragma unroll
+  for (int h = 0; h < kHalves; ++h) s[h] = f32x16{};
 #pragma unroll
   for (int kc = 0; kc < Shape<D>::kSteps; ++kc) {
-    const u32x4 a0 = *(const u32x4*)(cK + k_off<D>(x.l32, 2 * kc + x.hh));
-    const u32x4 a1 = *(const u32x4*)(cK + k_off<D>(32 + x.l32, 2 * kc + x.hh));
-    s0 = E::mma(a0, st.qf[kc], s0);
-    s1 = E::mma(a1, st.qf[kc], s1);
+#pragma unroll
+    for (int h = 0; h < kHalves; ++h) {
+      const u32x4 a = *(const u32x4*)(cK + k_off<D>(32 * h + x.l32, 2 * kc + x.hh));
+      s[h] = E::mma(a, st.qf[kc], s[h]);
+    }
   }
 }
 
@@ -228,17 +244,19 @@ __device__ __forceinline__ void tile_scores(const unsigned short* __restrict__ c
 // sequence end for some row of the wavefront: key kb + off is visible iff
 // 0 <= kb + off - vis_lo <= vis_span.
 template <int D>
-__device__ __forceinline__ void tile_mask(const LoopCtx<D>& x, int t, f32x16& s0, f32x16& s1) {
+__device__ __forceinline__ void tile_mask(const LoopCtx<D>& x, int t, f32x16 (&s)[kHalves]) {
   const int kb = t * kBC;
   const int ke = kb + kBC - 1;
   const bool need_mask = (ke >= x.N) || (x.causal && ke > x.wq0) || (x.wl >= 0 && kb < x.wq1 - x.wl);
   if (!need_mask) return;
   const int base = kb - x.vis_lo + 4 * x.hh;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int off = 8 * (i >> 2) + (i & 3);
-    s0[i] = ((unsigned)(base + off) <= x.vis_span) ? s0[i] : -INFINITY;
-    s1[i] = ((unsigned)(base + off + 32) <= x.vis_span) ? s1[i] : -INFINITY;
+  for (int h = 0; h < kHalves; ++h) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int off = 32 * h + 8 * (i >> 2) + (i & 3);
+      s[h][i] = ((unsigned)(base + off) <= x.vis_span) ? s[h][i] : -INFINITY;
+    }
   }
 }
 
@@ -247,38 +265,43 @@ __device__ __forceinline__ void tile_mask(const LoopCtx<D>& x, int t, f32x16& s0
 // reference max and sum, and returns the factor the partial output must be
 // multiplied by (1 unless the reference max moved).
 template <typename E, int D>
-__device__ __forceinline__ float tile_softmax(const LoopCtx<D>& x, RowState<D>& st, f32x16& s0, f32x16& s1,
+__device__ __forceinline__ float tile_softmax(const LoopCtx<D>& x, RowState<D>& st, f32x16 (&s)[kHalves],
                                               u32x4* pf) {
-  float mx = fmaxf(s0[0], s1[0]);
+  // row max over the lane's 16*kHalves scores (pairs fold into max3)
+  float mx = -INFINITY;
 #pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+  for (int h = 0; h < kHalves; ++h) {
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[h][i], s[h][i + 1]));
+  }
   float mlo, mhi;
   half_pair(mx, mlo, mhi);
   mx = fmaxf(mlo, mhi) * x.c;
-  // move the row's reference max only when the true max got ahead of it by
-  // more than the slack (always on the first visible key)
-  // (no NaN can arise: when bumped, mx is finite and m_use - mx is finite
-  // or -inf; otherwise the factor is exactly 1)
+  // Move the reference max only when the true max got ahead of it by more
+  // than the slack (always on the first visible key).  No NaN can arise:
+  // when bumped, mx is finite and m_use - mx is finite or -inf; otherwise
+  // the factor is exactly 1.
   const bool bump = mx > st.m_use + kRescaleSlack;
   const float alpha = bump ? __builtin_amdgcn_exp2f(st.m_use - mx) : 1.f;
-  const float m_new = bump ? mx : st.m_use;
-  st.m_use = m_new;
-  const float m_exp = (m_new == -INFINITY) ? 0.f : m_new;        // nothing visible yet
+  st.m_use = bump ? mx : st.m_use;
+  const float m_exp = (st.m_use == -INFINITY) ? 0.f : st.m_use;  // nothing visible yet
   float rs = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    s0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], x.c, -m_exp));
-    s1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], x.c, -m_exp));
-    rs += s0[i] + s1[i];
+  for (int h = 0; h < kHalves; ++h) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[h][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][i], x.c, -m_exp));
+      rs += s[h][i];
+    }
   }
   st.l_run = __builtin_fmaf(st.l_run, alpha, rs);
   // P^T operands: the lane's own probabilities, 8 keys per k-step
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    pf[j] = u32x4{E::pack2(s0[8 * j + 0], s0[8 * j + 1]), E::pack2(s0[8 * j + 2], s0[8 * j + 3]),
-                  E::pack2(s0[8 * j + 4], s0[8 * j + 5]), E::pack2(s0[8 * j + 6], s0[8 * j + 7])};
-    pf[2 + j] = u32x4{E::pack2(s1[8 * j + 0], s1[8 * j + 1]), E::pack2(s1[8 * j + 2], s1[8 * j + 3]),
-                      E::pack2(s1[8 * j + 4], s1[8 * j + 5]), E::pack2(s1[8 * j + 6], s1[8 * j + 7])};
+  for (int h = 0; h < kHalves; ++h) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      pf[2 * h + j] = u32x4{E::pack2(s[h][8 * j + 0], s[h][8 * j + 1]), E::pack2(s[h][8 * j + 2], s[h][8 * j + 3]),
+                            E::pack2(s[h][8 * j + 4], s[h][8 * j + 5]), E::pack2(s[h][8 * j + 6], s[h][8 * j + 7])};
   }
   return alpha;
 }
@@ -293,7 +316,7 @@ __device__ __forceinline__ void tile_pv(const unsigned short* __restrict__ vC, c
   for (int ct = 0; ct < Shape<D>::kOutTiles; ++ct) {
     const int col = 32 * ct + x.v_col_lane;
 #pragma unroll
-    for (int mc = 0; mc < 4; ++mc) {
+    for (int mc = 0; mc < 2 * kHalves; ++mc) {
       const int ra = 16 * mc + x.v_row_lane;
       const s16x4 lo = lds_read_tr(vC, v_off<D>(ra, col));
       const s16x4 hi = lds_read_tr(vC, v_off<D>(ra + 8, col));
@@ -319,9 +342,9 @@ __device__ __forceinline__ void rescale_if_needed(float alpha, f32x16* oacc, int
 //   2. softmax(S(t)) -> P(t), interleaved with O += P(t-1) V(t-1), after O is
 //      brought to the reference max that P(t-1) was computed with.
 // K(t) and V(t-1) are in LDS when the step starts.  The step first starts
-// copying V(t) into vN (V(t-2)'s buffer), then K(t+2) into kN (K(t-1)'s);
-// both buffers were last read in step t-1.  K thus travels two steps ahead,
-// V one.  The buffer pointers are restrict-qualified: copy targets are never
+// copying V into vN (V(t) with two V buffers, V(t+1) with three; the buffer
+// held V(t-2)), then K(t+2) into kN (K(t-1)'s buffer); both buffers were
+// last read in step t-1.  K thus travels two steps ahead, V one or two.  The buffer pointers are restrict-qualified: copy targets are never
 // read in this step, which lets the LDS reads proceed while copies are in
 // flight.
 template <typename E, int D, bool kHasPrev>
@@ -332,26 +355,27 @@ __device__ __forceinline__ void pipeline_step(const unsigned short* __restrict__
                                               const LoopCtx<D>& x, RowState<D>& st, u32x4* pf_prev,
                                               float& alpha_prev, int t) {
   using S = Shape<D>;
-  copy_tile_async<D>(x.rv, x.off.v, vN, t, x.wave);
-  copy_tile_async<D>(x.rk, x.off.k, kN, t + 2, x.wave);  // past the end: zeros, never read
+  // V(t) (two V buffers) or V(t+1) (three); past the end: zeros, never read
+  copy_tile_async<D>(x.rv, x.off.v, vN, t + kVBufs - 2, x.wave);
+  copy_tile_async<D>(x.rk, x.off.k, kN, t + 2, x.wave);
 
-  f32x16 s0, s1;
+  f32x16 s[kHalves];
   __builtin_amdgcn_s_setprio(2);
-  tile_scores<E, D>(kC, x, st, s0, s1);
+  tile_scores<E, D>(kC, x, st, s);
   __builtin_amdgcn_s_setprio(0);
-  tile_mask<D>(x, t, s0, s1);
+  tile_mask<D>(x, t, s);
 
   // P(t-1) was computed with the reference max as it stood after tile t-1;
   // O still carries the scale before it: bring O to that scale first.
   if (kHasPrev) rescale_if_needed(alpha_prev, st.oacc, S::kOutTiles);
 
-  u32x4 pf[4];
-  const float alpha = tile_softmax<E, D>(x, st, s0, s1, pf);
+  u32x4 pf[2 * kHalves];
+  const float alpha = tile_softmax<E, D>(x, st, s, pf);
   if (kHasPrev) {
     tile_pv<E, D>(vC, x, st, pf_prev);
     // interleave: each PV MFMA follows a slice of the softmax work, and its
     // two transposing reads were issued two MFMAs earlier
-    constexpr int kPv = 4 * S::kOutTiles;
+    constexpr int kPv = 2 * kHalves * S::kOutTiles;
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS read
 #pragma unroll
     for (int g = 0; g < kPv; ++g) {
@@ -361,7 +385,7 @@ __device__ __forceinline__ void pipeline_step(const unsigned short* __restrict__
     }
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) pf_prev[j] = pf[j];
+  for (int j = 0; j < 2 * kHalves; ++j) pf_prev[j] = pf[j];
   alpha_prev = alpha;
 }
 
@@ -377,7 +401,7 @@ __device__ __forceinline__ void tile_barrier() {
 }
 
 template <typename E, int D>
-__global__ void __launch_bounds__(kThreads, 2) fwd_mfma_kernel(FwdParams p) {
+__global__ void __launch_bounds__(kThreads, kWavesPerSimd) fwd_mfma_kernel(FwdParams p) {
   using S = Shape<D>;
   // three K and two V buffers, as separate objects (80 KiB at d = 128, so two
   // workgroups share a compute unit)
@@ -386,6 +410,11 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_mfma_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned short sK2[kBC * D];
   __shared__ __attribute__((aligned(16))) unsigned short sV0[kBC * D];
   __shared__ __attribute__((aligned(16))) unsigned short sV1[kBC * D];
+#if FA_V_BUFFERS == 3
+  __shared__ __attribute__((aligned(16))) unsigned short sV2[kBC * D];
+#else
+  unsigned short* const sV2 = sV0;  // never used with two V buffers
+#endif
 
   LoopCtx<D> x;
   const int tid = threadIdx.x;
@@ -448,25 +477,33 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_mfma_kernel(FwdParams p) {
   st.m_use = -INFINITY;
   st.l_run = 0.f;
 
-  // With i = t - t_beg: K(t) lives in K buffer i % 3, V(t) in V buffer i % 2.
+  // With i = t - t_beg: K(t) lives in K buffer i % 3, V(t) in V buffer
+  // i % kVBufs.
   // The step loop is unrolled six ways so every buffer choice is a
   // compile-time constant (LDS addresses fold into instruction offsets).
   auto kbuf = [&](int j) { return j == 0 ? sK0 : (j == 1 ? sK1 : sK2); };
-  auto vbuf = [&](int j) { return j == 0 ? sV0 : sV1; };
-  constexpr int kCopyLoads = S::kLoadsPerWave;  // loads per copy per wave
+  auto vbuf = [&](int j) { return j == 0 ? sV0 : (j == 1 ? sV1 : sV2); };
+  // copies a wave may leave in flight at a step's barrier: with two V
+  // buffers the previous step's K copy (its last), with three all of the
+  // previous step's copies
+  constexpr int kInFlight = (kVBufs - 1) * S::kLoadsPerWave;
   const int t0 = x.t_beg;
   copy_tile_async<D>(x.rk, x.off.k, sK0, t0, x.wave);
   copy_tile_async<D>(x.rk, x.off.k, sK1, t0 + 1, x.wave);  // past the end: zeros, never read
-  u32x4 pf_prev[4];
+  if (kVBufs == 3) copy_tile_async<D>(x.rv, x.off.v, sV0, t0, x.wave);
+  u32x4 pf_prev[2 * kHalves];
   float alpha_prev = 1.f;
   tile_barrier<0>();
-  pipeline_step<E, D, false>(sK0, sK2, sV1, sV0, x, st, pf_prev, alpha_prev, t0);
+  pipeline_step<E, D, false>(sK0, sK2, vbuf(kVBufs - 1), vbuf(kVBufs == 3 ? 1 : 0), x, st, pf_prev, alpha_prev,
+                             t0);
   auto step = [&](auto uc, int t) {
     constexpr int u = decltype(uc)::value;  // (t - t0) % 6
-    // everything but the previous step's K copy (its last) has landed
-    tile_barrier<kCopyLoads>();
-    pipeline_step<E, D, true>(kbuf(u % 3), kbuf((u + 2) % 3), vbuf((u + 1) % 2), vbuf(u % 2), x, st,
-                              pf_prev, alpha_prev, t);
+    // reads K(t) and V(t-1); fills the buffers of K(t-1) and V(t-2)
+    constexpr int vc = (u + kVBufs - 1) % kVBufs;
+    constexpr int vn = kVBufs == 3 ? (u + 1) % 3 : u % 2;
+    tile_barrier<kInFlight>();
+    pipeline_step<E, D, true>(kbuf(u % 3), kbuf((u + 2) % 3), vbuf(vc), vbuf(vn), x, st, pf_prev, alpha_prev,
+                              t);
   };
   for (int t = t0 + 1; t < x.t_end; t += 6) {
     step(std::integral_constant<int, 1>{}, t);
@@ -477,12 +514,15 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_mfma_kernel(FwdParams p) {
     if (t + 5 < x.t_end) step(std::integral_constant<int, 0>{}, t + 5);
   }
   // drain: P(t_end-1) V(t_end-1)
-  tile_barrier<kCopyLoads>();
+  tile_barrier<kInFlight>();
   rescale_if_needed(alpha_prev, st.oacc, S::kOutTiles);
-  if (((x.t_end - 1 - t0) & 1) == 0)
+  const int rl = (x.t_end - 1 - t0) % kVBufs;
+  if (rl == 0)
     tile_pv<E, D>(sV0, x, st, pf_prev);
-  else
+  else if (rl == 1)
     tile_pv<E, D>(sV1, x, st, pf_prev);
+  else
+    tile_pv<E, D>(sV2, x, st, pf_prev);
 
   // ---- epilogue: one division per row, store O and the logsumexp
   float llo, lhi;
