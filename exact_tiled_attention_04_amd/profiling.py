@@ -145,9 +145,12 @@ def main():
         for k, v in sorted(a.items()):
             lines.append(f"  {k:34s} {statistics.mean(v):.6g}")
         if "SQ_VALU_MFMA_BUSY_CYCLES" in a and "GRBM_GUI_ACTIVE" in a:
+            # GRBM_GUI_ACTIVE comes back summed over the 8 XCDs: one XCD's
+            # count is the kernel's duration in GPU clocks
             simd = 256 * 4
-            util = statistics.mean(a["SQ_VALU_MFMA_BUSY_CYCLES"]) / (statistics.mean(a["GRBM_GUI_ACTIVE"]) * simd)
-            lines.append(f"  MFMA busy / (GUI active x 1024 SIMDs) = {100 * util:.1f}%")
+            gui = statistics.mean(a["GRBM_GUI_ACTIVE"]) / 8
+            util = statistics.mean(a["SQ_VALU_MFMA_BUSY_CYCLES"]) / (gui * simd)
+            lines.append(f"  MFMA busy cycles / (GPU-active cycles per XCD x 1024 SIMDs) = {100 * util:.1f}%")
         if "SQ_LDS_BANK_CONFLICT" in a and "SQ_LDS_IDX_ACTIVE" in a:
             bc = statistics.mean(a["SQ_LDS_BANK_CONFLICT"]) / max(1.0, statistics.mean(a["SQ_LDS_IDX_ACTIVE"]))
             lines.append(f"  LDS bank-conflict cycles / LDS active cycles = {100 * bc:.2f}%")
