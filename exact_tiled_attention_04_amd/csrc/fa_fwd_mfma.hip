@@ -196,6 +196,9 @@ __device__ __forceinline__ void copy_tile_async(__amdgpu_buffer_rsrc_t r, const 
 
 constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 
+// PV MFMAs by which the transposing V reads run ahead of their MFMA.
+constexpr int kPvReadLead = 4;
+
 // A row's running max may lag the true max by up to this much (log2 units)
 // before the partial output is rescaled; probabilities then stay <= 2^8.
 constexpr float kRescaleSlack = 8.0f;
@@ -260,6 +263,26 @@ __device__ __forceinline__ void tile_mask(const LoopCtx<D>& x, int t, f32x16 (&s
   }
 }
 
+// Maximum of N values as a tree of three-input maxima (v_max3_f32): every
+// level folds groups of three and carries up to two leftovers, so 32 values
+// take 16 instructions instead of 31 two-input ones.
+template <int N>
+__device__ __forceinline__ float max_tree(const float (&a)[N]) {
+  if constexpr (N == 1) {
+    return a[0];
+  } else if constexpr (N == 2) {
+    return __builtin_fmaxf(a[0], a[1]);
+  } else {
+    constexpr int G = N / 3, M = G + N % 3;
+    float b[M];
+#pragma unroll
+    for (int i = 0; i < G; ++i) b[i] = __builtin_fmaxf(__builtin_fmaxf(a[3 * i], a[3 * i + 1]), a[3 * i + 2]);
+#pragma unroll
+    for (int i = 0; i < N % 3; ++i) b[G + i] = a[3 * G + i];
+    return max_tree<M>(b);
+  }
+}
+
 // Online softmax of one score tile (base 2, scale folded into the
 // exponent): turns s0/s1 into the P^T operands pf, updates the row's
 // reference max and sum, and returns the factor the partial output must be
@@ -267,13 +290,14 @@ __device__ __forceinline__ void tile_mask(const LoopCtx<D>& x, int t, f32x16 (&s
 template <typename E, int D>
 __device__ __forceinline__ float tile_softmax(const LoopCtx<D>& x, RowState<D>& st, f32x16 (&s)[kHalves],
                                               u32x4* pf) {
-  // row max over the lane's 16*kHalves scores (pairs fold into max3)
-  float mx = -INFINITY;
+  // row max over the lane's 16*kHalves scores
+  float sv[16 * kHalves];
 #pragma unroll
   for (int h = 0; h < kHalves; ++h) {
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[h][i], s[h][i + 1]));
+    for (int i = 0; i < 16; ++i) sv[16 * h + i] = s[h][i];
   }
+  float mx = max_tree(sv);
   float mlo, mhi;
   half_pair(mx, mlo, mhi);
   mx = fmaxf(mlo, mhi) * x.c;
@@ -374,12 +398,12 @@ __device__ __forceinline__ void pipeline_step(const unsigned short* __restrict__
   if (kHasPrev) {
     tile_pv<E, D>(vC, x, st, pf_prev);
     // interleave: each PV MFMA follows a slice of the softmax work, and its
-    // two transposing reads were issued two MFMAs earlier
+    // two transposing reads were issued kPvReadLead MFMAs earlier
     constexpr int kPv = 2 * kHalves * S::kOutTiles;
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvReadLead, 0);  // LDS read
 #pragma unroll
     for (int g = 0; g < kPv; ++g) {
-      if (g + 2 < kPv) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+      if (g + kPvReadLead < kPv) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);                    // VALU
     }
