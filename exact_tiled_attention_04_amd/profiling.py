@@ -108,7 +108,7 @@ def main():
     lines += [f"    {c}" for c in args.command]
     lines += ["", f"kernel: `{tr['kernel']}`",
               f"grid {tr['grid']} work-items, workgroup {tr['workgroup']}, LDS {tr['lds_bytes']} B, "
-              f"VGPR {tr['vgpr']}, AGPR {tr['agpr']}", "",
+              f"trace fields VGPR_Count {tr['vgpr']}, Accum_VGPR_Count {tr['agpr']} (the compiler's resource report is the authority on register use)", "",
               f"kernel trace, last {tr['dispatches']} dispatches: avg {tr['avg_us']:.1f} us, "
               f"min {tr['min_us']:.1f} us, max {tr['max_us']:.1f} us"]
     if args.flops:
