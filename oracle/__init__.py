@@ -14,6 +14,10 @@ Contents
 ``online_emul``    the tiled method itself in fp64: query and key/value blocks,
                    a running max and running sum per row, rescaling of the
                    partial output, one division at the end.
+``attention_bwd_ref``  fp64 gradients dQ, dK, dV of the forward above for an
+                   upstream gradient dO (chain rule through O = P V and the
+                   row softmax; P rebuilt per block of rows), with optional
+                   absolute-value products for error bounds.
 
 What is computed (all three): for batch b, query head h with key/value head
 h_kv = h // (Hq // Hkv), and query row i,
@@ -36,8 +40,11 @@ with its justification in the design notes at the repository root.
 
 Every function here is pinned by tests in ``tests/test_oracle.py`` against
 closed forms, invariants, hand-worked fixtures and an independent library
-routine (torch's CPU scaled-dot-product attention in float64).
+routine (torch's CPU scaled-dot-product attention in float64); the gradients
+are pinned in ``tests/test_oracle_bwd.py`` against central finite differences
+of the forward oracle, torch's float64 autograd, and closed forms.
 """
 from .attention_ref import attention_fwd, masked, kv_head_of  # noqa: F401
 from .twopass_ref import attention_twopass  # noqa: F401
 from .online_emul import attention_online  # noqa: F401
+from .attention_bwd_ref import attention_bwd  # noqa: F401

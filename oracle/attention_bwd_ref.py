@@ -1,0 +1,155 @@
+"""Plain fp64 gradients of exact attention (test infrastructure only).
+
+What is differentiated is the forward of ``attention_ref``: for batch b, query
+head h (key/value head h_kv = h // (Hq // Hkv)) and query row i,
+
+    s_ij = scale * <q_i, k_j>,   s_ij = -inf where masked,
+    p_ij = softmax_j(s_ij),      o_i = sum_j p_ij v_j.
+
+Given an upstream gradient dO of the output (the logsumexp output carries no
+upstream gradient), the chain rule gives, per (b, h),
+
+    dV   = P^T dO                       (o is linear in v)
+    dP   = dO V^T                       (dL/dp_ij = <do_i, v_j>)
+    dS   = P * (dP - rowsum(P * dP))    (Jacobian of a row softmax)
+    dQ   = scale * dS K
+    dK   = scale * dS^T Q
+
+and a key/value head shared by a group of query heads collects the dK and dV
+of every head in its group (the same K/V rows enter each of those heads'
+forward).  Masked pairs have p_ij = 0, so they contribute nothing anywhere.
+
+This is the backward pass the Flash Attention page alludes to in its tiling
+section ("recomputation": the probabilities are rebuilt from Q, K and the
+saved row statistics instead of being stored); the oracle simply materialises
+P per block of query rows, over every key, in fp64.  The pages print no
+backward formulas: the ones above are the derivative of the forward, which is
+the plainest reading of "the gradient of exact attention".
+
+Optionally the function also returns, for error bounds in tests, the same
+products taken over absolute values (|P|^T |dO|, scale |dS| |K|,
+scale |dS|^T |Q|) and the row terms F_i = sum_c |do_ic| |o_ic| with their
+products scale (P * F) |K| and scale (P * F)^T |Q|.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional
+
+import numpy as np
+
+from .attention_ref import kv_head_of, masked
+
+ROW_BLOCK = 256
+
+
+def _one_kv_head(qs, kh, vh, dos, causal, window_left, scale, bounds):
+    """Gradients for one (batch, key/value head) and the query heads of its
+    group.  qs, dos: [G, N, d] fp64; kh, vh: [N, d] fp64.  Returns dq [G, N, d],
+    dk [N, d], dv [N, d] and, if bounds, a dict of magnitude terms."""
+    G, N, d = qs.shape
+    keys = np.arange(N)
+    dq = np.zeros((G, N, d))
+    dk = np.zeros((N, d))
+    dv = np.zeros((N, d))
+    mag = None
+    if bounds:
+        mag = {"dq": np.zeros((G, N, d)), "dk": np.zeros((N, d)), "dv": np.zeros((N, d)),
+               "dq_f": np.zeros((G, N, d)), "dk_f": np.zeros((N, d))}
+    for g in range(G):
+        qh, doh = qs[g], dos[g]
+        for s0 in range(0, N, ROW_BLOCK):
+            r = np.arange(s0, min(N, s0 + ROW_BLOCK))
+            # recompute the probabilities of these rows against every key
+            S = scale * (qh[r] @ kh.T)
+            S[masked(r[:, None], keys[None, :], causal, window_left)] = -np.inf
+            m = S.max(axis=1, keepdims=True)
+            E = np.exp(S - m)
+            P = E / E.sum(axis=1, keepdims=True)
+            # chain rule through O = P V and the row softmax
+            dv += P.T @ doh[r]
+            dP = doh[r] @ vh.T
+            rowdot = (P * dP).sum(axis=1, keepdims=True)
+            dS = P * (dP - rowdot)
+            dq[g, r] = scale * (dS @ kh)
+            dk += scale * (dS.T @ qh[r])
+            if bounds:
+                A = np.abs(dS)
+                mag["dv"] += P.T @ np.abs(doh[r])
+                mag["dq"][g, r] = scale * (A @ np.abs(kh))
+                mag["dk"] += scale * (A.T @ np.abs(qh[r]))
+                O = P @ vh
+                F = (np.abs(doh[r]) * np.abs(O)).sum(axis=1, keepdims=True)
+                PF = P * F
+                mag["dq_f"][g, r] = scale * (PF @ np.abs(kh))
+                mag["dk_f"] += scale * (PF.T @ np.abs(qh[r]))
+    return dq, dk, dv, mag
+
+
+def attention_bwd(q, k, v, do, causal: bool = False, window_left: int = -1,
+                  scale: Optional[float] = None, threads: Optional[int] = None,
+                  bounds: bool = False):
+    """Exact attention gradients in float64.
+
+    q, do: [B, Hq, N, d]; k, v: [B, Hkv, N, d] (any float dtype; widened to
+    fp64).  Returns (dq [B, Hq, N, d], dk [B, Hkv, N, d], dv [B, Hkv, N, d]),
+    plus a dict of magnitude terms (same keys as the gradients, and 'dq_f',
+    'dk_f'; shapes as the gradient they bound) when bounds=True.
+
+    Raises ValueError on inconsistent shapes, Hq not a multiple of Hkv, or
+    window_left < -1.
+    """
+    q, k, v, do = (np.asarray(x) for x in (q, k, v, do))
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4 or do.shape != q.shape:
+        raise ValueError("q, do must be [B, Hq, N, d] and k, v [B, Hkv, N, d]")
+    B, Hq, N, d = q.shape
+    Bk, Hkv, Nk, dk_ = k.shape
+    if (Bk, Nk, dk_) != (B, N, d) or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    if Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError("Hq must be a positive multiple of Hkv")
+    if window_left < -1:
+        raise ValueError("window_left must be >= -1")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    scale = float(scale)
+    G = Hq // Hkv
+    dq = np.zeros((B, Hq, N, d))
+    dk = np.zeros((B, Hkv, N, d))
+    dv = np.zeros((B, Hkv, N, d))
+    mags = None
+    if bounds:
+        mags = {"dq": np.zeros_like(dq), "dk": np.zeros_like(dk), "dv": np.zeros_like(dv),
+                "dq_f": np.zeros_like(dq), "dk_f": np.zeros_like(dk)}
+    if B * Hq * N == 0:
+        return (dq, dk, dv, mags) if bounds else (dq, dk, dv)
+
+    def work(bk):
+        b, hk = divmod(bk, Hkv)
+        heads = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == hk]
+        qs = np.stack([q[b, h].astype(np.float64) for h in heads])
+        dos = np.stack([do[b, h].astype(np.float64) for h in heads])
+        gq, gk, gv, mag = _one_kv_head(qs, k[b, hk].astype(np.float64), v[b, hk].astype(np.float64), dos,
+                                       causal, window_left, scale, bounds)
+        for gi, h in enumerate(heads):
+            dq[b, h] = gq[gi]
+            if bounds:
+                mags["dq"][b, h] = mag["dq"][gi]
+                mags["dq_f"][b, h] = mag["dq_f"][gi]
+        dk[b, hk] = gk
+        dv[b, hk] = gv
+        if bounds:
+            mags["dk"][b, hk] = mag["dk"]
+            mags["dv"][b, hk] = mag["dv"]
+            mags["dk_f"][b, hk] = mag["dk_f"]
+
+    nthreads = threads or len(os.sched_getaffinity(0))
+    nthreads = max(1, min(nthreads, B * Hkv))
+    if nthreads == 1:
+        for bk in range(B * Hkv):
+            work(bk)
+    else:
+        with ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(work, range(B * Hkv)))
+    return (dq, dk, dv, mags) if bounds else (dq, dk, dv)
