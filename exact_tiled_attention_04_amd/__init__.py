@@ -1,10 +1,12 @@
-"""Exact attention forward (IO-aware, tiled, online softmax) for AMD MI355X.
+"""Exact attention forward and backward (IO-aware, tiled, online softmax) for
+AMD MI355X.
 
 The computation lives in ``libfa.so`` (HIP kernels for gfx950 behind the C ABI
 of ``include/fa.h``).  This package is a thin binding:
 
     _lib        the C entry points under their C names (raw addresses, sizes)
-    attention   ``fwd(q, k, v, causal, window_left, scale)`` on torch tensors
+    attention   ``fwd(q, k, v, causal, window_left, scale)`` and
+                ``bwd(q, k, v, o, lse, dout, ...)`` on torch tensors
     build       compiles libfa.so in-tree with hipcc
 """
 from ._lib import FaError, LIB_PATH, load  # noqa: F401
@@ -15,4 +17,9 @@ def fwd(*args, **kwargs):
     return _fwd(*args, **kwargs)
 
 
-__all__ = ["fwd", "FaError", "LIB_PATH", "load"]
+def bwd(*args, **kwargs):
+    from .attention import bwd as _bwd
+    return _bwd(*args, **kwargs)
+
+
+__all__ = ["fwd", "bwd", "FaError", "LIB_PATH", "load"]

@@ -22,8 +22,8 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_MISALIGNED = -3
 FA_ERR_HIP = -4
 
-EXPORTED = ["fa_fwd", "fa_fwd_bf16", "fa_fwd_f16", "fa_fwd_f32", "fa_status_string",
-            "fa_last_error", "fa_version"]
+EXPORTED = ["fa_fwd", "fa_fwd_bf16", "fa_fwd_f16", "fa_fwd_f32", "fa_bwd", "fa_bwd_bf16", "fa_bwd_f16",
+            "fa_bwd_workspace_size", "fa_status_string", "fa_last_error", "fa_version"]
 
 _lock = threading.Lock()
 _lib = None
@@ -55,6 +55,15 @@ def load() -> ctypes.CDLL:
             fn.restype = I
         lib.fa_fwd.argtypes = fwd_args + [I]
         lib.fa_fwd.restype = I
+        bwd_args = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
+        for name in ("fa_bwd_bf16", "fa_bwd_f16"):
+            fn = getattr(lib, name)
+            fn.argtypes = bwd_args
+            fn.restype = I
+        lib.fa_bwd.argtypes = bwd_args + [I]
+        lib.fa_bwd.restype = I
+        lib.fa_bwd_workspace_size.argtypes = [I, I, I]
+        lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
         lib.fa_status_string.argtypes = [I]
         lib.fa_status_string.restype = ctypes.c_char_p
         lib.fa_last_error.argtypes = []
@@ -87,6 +96,31 @@ def fa_fwd_f16(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window_left, scale, st
 def fa_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window_left, scale, stream) -> int:
     return load().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
                              int(bool(causal)), window_left, scale, _ptr(stream))
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, causal, window_left, scale, stream,
+           dtype) -> int:
+    return load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                         _ptr(workspace), B, Hq, Hkv, N, d, int(bool(causal)), window_left, scale, _ptr(stream),
+                         dtype)
+
+
+def fa_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, causal, window_left, scale,
+                stream) -> int:
+    return load().fa_bwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                              _ptr(dv), _ptr(workspace), B, Hq, Hkv, N, d, int(bool(causal)), window_left, scale,
+                              _ptr(stream))
+
+
+def fa_bwd_f16(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, causal, window_left, scale,
+               stream) -> int:
+    return load().fa_bwd_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                             _ptr(dv), _ptr(workspace), B, Hq, Hkv, N, d, int(bool(causal)), window_left, scale,
+                             _ptr(stream))
+
+
+def fa_bwd_workspace_size(B: int, Hq: int, N: int) -> int:
+    return load().fa_bwd_workspace_size(B, Hq, N)
 
 
 def fa_status_string(status: int) -> str:

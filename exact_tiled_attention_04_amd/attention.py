@@ -56,3 +56,57 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     if status != _lib.FA_OK:
         raise _lib.FaError(status, _lib.fa_last_error())
     return o, lse
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+        dout: torch.Tensor, causal: bool = False, window_left: int = -1, scale: Optional[float] = None,
+        dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None,
+        stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Gradients of ``fwd``'s output with respect to q, k and v on the GPU.
+
+    q, k, v, causal, window_left, scale: as passed to ``fwd``; o, lse: what
+    ``fwd`` returned for them; dout: upstream gradient like o.  Only float16
+    and bfloat16 are supported.  Returns (dq, dk, dv) like (q, k, v).  The
+    float32 workspace (``_lib.fa_bwd_workspace_size`` bytes) is allocated here
+    unless given.  Asynchronous on ``stream`` (default: the current stream).
+    Raises _lib.FaError when the library rejects the arguments.
+    """
+    ts = (q, k, v, o, dout)
+    if any(t.dim() != 4 for t in ts):
+        raise ValueError("q, k, v, o, dout must be [B, H, N, d]")
+    if q.dtype not in (torch.float16, torch.bfloat16) or any(t.dtype != q.dtype for t in ts):
+        raise ValueError("q, k, v, o, dout must share one dtype, float16 or bfloat16")
+    if not q.is_cuda or any(t.device != q.device for t in ts + (lse,)):
+        raise ValueError("all tensors must be on one GPU")
+    if not all(t.is_contiguous() for t in ts + (lse,)):
+        raise ValueError("all tensors must be contiguous")
+    B, Hq, N, d = q.shape
+    if tuple(k.shape) != (B, k.shape[1], N, d) or k.shape != v.shape:
+        raise ValueError("k and v must be [B, Hkv, N, d] with q's B, N, d")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must be shaped like q")
+    if lse.shape != (B, Hq, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, Hq, N]")
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = dq if dq is not None else torch.empty_like(q)
+    dk = dk if dk is not None else torch.empty_like(k)
+    dv = dv if dv is not None else torch.empty_like(v)
+    for name, g, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if g.shape != ref.shape or g.dtype != ref.dtype or not g.is_contiguous() or g.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like its input")
+    nbytes = _lib.fa_bwd_workspace_size(B, Hq, N)
+    if workspace is None:
+        workspace = torch.empty(max(1, nbytes // 4), dtype=torch.float32, device=q.device)
+    if workspace.dtype != torch.float32 or workspace.numel() * 4 < nbytes or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous float32 tensor of at least {nbytes} bytes")
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        status = _lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                             dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                             B, Hq, Hkv, N, d, causal, window_left, float(scale), s.cuda_stream, _DTYPES[q.dtype])
+    if status != _lib.FA_OK:
+        raise _lib.FaError(status, _lib.fa_last_error())
+    return dq, dk, dv

@@ -1,0 +1,491 @@
+// Exact attention backward (dQ, dK, dV), bf16/fp16 inputs, on CDNA4 matrix
+// cores (gfx950).
+//
+// Given the forward's inputs, its output O and row logsumexp, and an upstream
+// gradient dO, the gradients of standard attention are (per batch and query
+// head, key/value head g(h)):
+//
+//   P    = exp(scale * Q K^T - lse)     recomputed, never stored
+//   dV  += P^T dO                       (summed over the query heads of g)
+//   dP   = dO V^T
+//   dS   = P * (dP - D),   D_i = sum_c dO_ic O_ic
+//   dQ   = scale * dS K
+//   dK  += scale * dS^T Q               (summed over the query heads of g)
+//
+// The probabilities are rebuilt from Q, K and the saved row statistics rather
+// than kept from the forward: the recomputation that the Flash Attention page
+// (heepie.pages.dev, tiling section) credits with trading a few extra FLOPs for
+// far less HBM traffic.  D_i uses the forward's output: for exact O it equals
+// sum_j P_ij dP_ij, the row term of the softmax Jacobian.
+//
+// Three launches, no atomics, bit-reproducible:
+//   1. prep: D_i and lse_i * log2(e) for every row, into the caller's
+//      workspace;
+//   2. dK/dV: one workgroup per (batch, key/value head, block of 128 keys);
+//      each of its 4 wavefronts owns 32 keys and keeps their K and V rows in
+//      registers as MFMA operands and their dK^T, dV^T in accumulators, while
+//      64-row tiles of Q, dO, lse, D of every query head in the group stream
+//      through LDS;
+//   3. dQ: one workgroup per (batch, query head, block of 128 queries), the
+//      forward's layout: each wavefront owns 32 queries, 64-key tiles of K and
+//      V stream through LDS.
+//
+// Matrix-core mapping as in the forward (v_mfma_f32_32x32x16; lane l holds
+// A[l%32][8*(l/32)+j], B[8*(l/32)+j][l%32], C[8*(i/4)+4*(l/32)+i%4][l%32]):
+// every product keeps the wavefront's own rows on the accumulator columns, so
+// a score accumulator is directly the B operand of the next product after
+// exp2 and rounding, and the streamed tile enters that product through the
+// transposing LDS read with the k order permuted to match the accumulator.
+// Streamed tiles are read both as 16-byte rows (A operand of a score-like
+// product) and through the transposing read, so their LDS swizzle is chosen
+// to be conflict-free for both patterns.
+#include "fa_internal.h"
+#include "fa_mfma_common.h"
+
+namespace fa {
+namespace {
+
+using namespace mfma;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaveSize * kWaves;
+constexpr int kRows = 32;                // rows a wavefront owns (queries in dQ, keys in dK/dV)
+constexpr int kBlock = kWaves * kRows;   // rows a workgroup owns
+constexpr int kTile = 64;                // streamed rows per LDS tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D>
+struct Shape {
+  static constexpr int kChunks = D / 8;     // 16-byte chunks per row
+  static constexpr int kSteps = D / 16;     // MFMA k-steps over the head dimension
+  static constexpr int kOutTiles = D / 32;  // 32-wide output tiles over the head dimension
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows per 1-KiB wave-wide load
+  static constexpr int kLoadsPerWave = kTile / kRowsPerLoad / kWaves;
+  static_assert(kTile % (kRowsPerLoad * kWaves) == 0, "tile must split evenly over the wavefronts");
+};
+
+// Chunk swizzle of a streamed tile.  Row reads: 16 lanes on 16 consecutive
+// rows, one logical chunk; transposing reads: 32 lanes on 4 consecutive rows
+// (starting at a multiple of 4) x 4 consecutive chunks.  Both hit 64 distinct
+// banks (checked with a bank model): D = 128 (256-byte rows) permutes the
+// chunk by the two low row bits into the high chunk bits and the next two row
+// bits into the low ones; D = 64 (128-byte rows) does the same with row bit 1
+// and row bits 2-3.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+template <int D>
+__device__ __forceinline__ int row_off(int row, int chunk) {  // element offset of a 16-byte chunk
+  return row * D + ((chunk ^ swz<D>(row)) << 3);
+}
+template <int D>
+__device__ __forceinline__ int tr_off(int row, int col) {  // element offset of a 4-element piece
+  return row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7);
+}
+
+// Per-lane source offsets of this lane's part of a tile copy: lane l fills
+// LDS bytes 16l..16l+15 of its 1-KiB piece, i.e. physical chunk l % kChunks
+// of its row, so it fetches the logical chunk the swizzle maps there.
+template <int D>
+struct CopyOffsets {
+  int off[Shape<D>::kLoadsPerWave];
+  __device__ __forceinline__ void init(int wave, int lane) {
+    using S = Shape<D>;
+#pragma unroll
+    for (int u = 0; u < S::kLoadsPerWave; ++u) {
+      const int piece = wave * S::kLoadsPerWave + u;
+      const int row = piece * S::kRowsPerLoad + lane / S::kChunks;
+      const int pch = lane % S::kChunks;
+      off[u] = row * S::kRowBytes + ((pch ^ swz<D>(row)) << 4);
+    }
+  }
+};
+
+// Copy rows row0 .. row0+kTile-1 of the tensor behind `r` (bounded to the
+// head's N rows: rows past the end arrive as zeros) straight into LDS.
+template <int D>
+__device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t r, const CopyOffsets<D>& c,
+                                          unsigned short* dst, int row0, int wave) {
+  using S = Shape<D>;
+  // (builtin arguments go through plain ints: the host compilation pass
+  // rejects template-dependent expressions in this builtin's operands)
+  const int soff = row0 * S::kRowBytes;
+#pragma unroll
+  for (int u = 0; u < S::kLoadsPerWave; ++u) {
+    const int piece = wave * S::kLoadsPerWave + u;
+    const int voff = c.off[u];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + piece * 512), 16, voff, soff, 0, 0);
+  }
+}
+
+// Copy kTile floats (rows row0.. of a bounded per-head vector) into LDS:
+// one 4-byte load per lane of one wavefront.
+__device__ __forceinline__ void copy_vec(__amdgpu_buffer_rsrc_t r, float* dst, int row0, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 4, 4 * lane, 4 * row0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, long long byte_off, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)base + byte_off), 0, bytes, kBufferFlags);
+}
+
+// Wait for every copy this wave issued, then for every wave.
+__device__ __forceinline__ void barrier_all() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// A = the streamed tile read through the transposing load for k-step mc
+// (rows 16mc..16mc+15 in the accumulator's order) and output tile ct.
+template <int D>
+__device__ __forceinline__ u32x4 tr_operand(const unsigned short* __restrict__ t, int mc, int ct, int row_lane,
+                                            int col_lane) {
+  const int ra = 16 * mc + row_lane;
+  const int col = 32 * ct + col_lane;
+  const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr(t, tr_off<D>(ra, col)));
+  const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(t, tr_off<D>(ra + 8, col)));
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// 32 x 32 product of 32 streamed rows (32h..32h+31 of the tile, read as
+// 16-byte rows) with the wavefront's own rows held as B operands.
+template <typename E, int D>
+__device__ __forceinline__ f32x16 rows_times_own(const unsigned short* __restrict__ t, int h, int l32, int hh,
+                                                 const u32x4* own) {
+  f32x16 acc = f32x16{};
+#pragma unroll
+  for (int kc = 0; kc < Shape<D>::kSteps; ++kc) {
+    const u32x4 a = *(const u32x4*)(t + row_off<D>(32 * h + l32, 2 * kc + hh));
+    acc = E::mma(a, own[kc], acc);
+  }
+  return acc;
+}
+
+// Load a row of 16-bit elements as the wavefront's B operands (lane holds
+// elements 16kc + 8hh .. +7 for k-step kc); zero past the end.
+template <int D>
+__device__ __forceinline__ void load_own_row(const unsigned short* row, bool valid, int hh, u32x4* dst) {
+#pragma unroll
+  for (int kc = 0; kc < Shape<D>::kSteps; ++kc)
+    dst[kc] = valid ? *(const u32x4*)(row + 16 * kc + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Store an accumulated output row (lane owns the row; element i of tile ct is
+// column 32ct + 8(i/4) + 4hh + i%4), multiplied by `mul`.
+template <typename E, int D>
+__device__ __forceinline__ void store_row(unsigned short* row, const f32x16* acc, float mul, int hh) {
+#pragma unroll
+  for (int ct = 0; ct < Shape<D>::kOutTiles; ++ct) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const u32x2 w = u32x2{E::pack2(acc[ct][4 * gq + 0] * mul, acc[ct][4 * gq + 1] * mul),
+                            E::pack2(acc[ct][4 * gq + 2] * mul, acc[ct][4 * gq + 3] * mul)};
+      *(u32x2*)(row + 32 * ct + 8 * gq + 4 * hh) = w;
+    }
+  }
+}
+
+// Pack the 16 fp32 values of one 32-row accumulator into the two B operands
+// of the k-steps it covers.
+template <typename E>
+__device__ __forceinline__ void pack_operands(const float* x, u32x4* dst) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    dst[j] = u32x4{E::pack2(x[8 * j + 0], x[8 * j + 1]), E::pack2(x[8 * j + 2], x[8 * j + 3]),
+                   E::pack2(x[8 * j + 4], x[8 * j + 5]), E::pack2(x[8 * j + 6], x[8 * j + 7])};
+}
+
+// ---------------------------------------------------------------------------
+// 1. Row terms: D_i = sum_c dO_ic O_ic (fp32) and lse_i * log2(e).
+
+template <typename E>
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b);
+
+template <>
+__device__ __forceinline__ float dot8<Bf16>(u32x4 a, u32x4 b) {
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    s = __builtin_fmaf(__uint_as_float(a[w] << 16), __uint_as_float(b[w] << 16), s);
+    s = __builtin_fmaf(__uint_as_float(a[w] & 0xffff0000u), __uint_as_float(b[w] & 0xffff0000u), s);
+  }
+  return s;
+}
+
+template <>
+__device__ __forceinline__ float dot8<F16>(u32x4 a, u32x4 b) {
+  // (the whole 16 bytes are reinterpreted at once: casting single elements
+  // of the dword vector compiled to reads of element 0 only)
+  const f16x8 x = __builtin_bit_cast(f16x8, a);
+  const f16x8 y = __builtin_bit_cast(f16x8, b);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s = __builtin_fmaf((float)x[e], (float)y[e], s);
+  return s;
+}
+
+template <typename E, int D>
+__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
+  constexpr int kLanesPerRow = D / 8;
+  constexpr int kRowsPerBlock = 256 / kLanesPerRow;
+  const long long row = (long long)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
+  const int c = threadIdx.x % kLanesPerRow;
+  float s = 0.f;
+  if (row < p.rows) {
+    const u32x4 a = *((const u32x4*)((const unsigned short*)p.dout + row * D) + c);
+    const u32x4 b = *((const u32x4*)((const unsigned short*)p.o + row * D) + c);
+    s = dot8<E>(a, b);
+  }
+#pragma unroll
+  for (int m = kLanesPerRow / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, kLanesPerRow);
+  if (row < p.rows && c == 0) {
+    p.delta[row] = s;
+    p.lse2[row] = p.lse[row] * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK, dV: workgroup = (batch, key/value head, 128 keys).
+
+template <typename E, int D>
+__global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p) {
+  using S = Shape<D>;
+  __shared__ __attribute__((aligned(16))) unsigned short sQ[2][kTile * D];
+  __shared__ __attribute__((aligned(16))) unsigned short sO[2][kTile * D];  // dO tiles
+  __shared__ __attribute__((aligned(16))) float sL[2][kTile];               // lse * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[2][kTile];               // D
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWaveSize - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWaveSize);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int g16 = lane >> 4, gi = lane & 15;
+  const int row_lane = 4 * hh + (gi >> 2), col_lane = 16 * (g16 & 1) + 4 * (gi & 3);
+
+  // work item: heavy first (with a causal mask the first key blocks see the most queries)
+  const int L = xcd_slice_index(blockIdx.x, p.items_dkv);
+  const int bk = L / p.n_blocks;
+  const int kb = L - bk * p.n_blocks;
+  const int b = bk / p.Hkv;
+  const int hk = bk - b * p.Hkv;
+  const int N = p.N;
+  const int k0 = kb * kBlock;
+  const int kw0 = k0 + wave * kRows;
+  const int myk = kw0 + l32;
+  const long long kv_head = ((long long)b * p.Hkv + hk) * N * D;
+
+  u32x4 kf[S::kSteps], vf[S::kSteps];
+  load_own_row<D>((const unsigned short*)p.k + kv_head + (long long)myk * D, myk < N, hh, kf);
+  load_own_row<D>((const unsigned short*)p.v + kv_head + (long long)myk * D, myk < N, hh, vf);
+  f32x16 dk[S::kOutTiles], dv[S::kOutTiles];
+#pragma unroll
+  for (int ct = 0; ct < S::kOutTiles; ++ct) dk[ct] = dv[ct] = f32x16{};
+
+  // queries that see some key of the block: causal from k0 on, a window up
+  // to the last key + window_left
+  const int wl = p.window_left;
+  const int k_last = min(N - 1, k0 + kBlock - 1);
+  const int q_lo = p.causal ? k0 : 0;
+  const int q_hi = wl >= 0 ? min(N - 1, k_last + wl) : N - 1;
+  const int t_lo = q_lo / kTile, t_hi = q_hi / kTile;
+  const int n_t = t_hi - t_lo + 1;
+  const int n_tiles = p.group * n_t;  // (query head in group, query tile)
+
+  // visible queries of this lane's key form [vq_lo, vq_lo + vq_span]
+  const int vq_lo = myk < N ? (p.causal ? myk : 0) : 0x3fffffff;
+  const unsigned vq_span = myk < N ? (unsigned)((wl >= 0 ? min(N - 1, myk + wl) : N - 1) - vq_lo) : 0u;
+  const int wk_last = min(N - 1, kw0 + kRows - 1);
+
+  CopyOffsets<D> co;
+  co.init(wave, lane);
+  const int head_bytes = N * S::kRowBytes;
+  auto issue = [&](int tau, int buf) {
+    const int g = tau / n_t;
+    const int q0 = (t_lo + tau - g * n_t) * kTile;
+    const long long bh = (long long)b * p.Hq + hk * p.group + g;
+    copy_tile<D>(head_rsrc(p.q, 2 * bh * N * D, head_bytes), co, sQ[buf], q0, wave);
+    copy_tile<D>(head_rsrc(p.dout, 2 * bh * N * D, head_bytes), co, sO[buf], q0, wave);
+    if (wave == 0) copy_vec(head_rsrc(p.lse2, 4 * bh * N, 4 * N), sL[buf], q0, lane);
+    if (wave == 1) copy_vec(head_rsrc(p.delta, 4 * bh * N, 4 * N), sD[buf], q0, lane);
+  };
+
+  issue(0, 0);
+  barrier_all();
+  for (int tau = 0; tau < n_tiles; ++tau) {
+    const int buf = tau & 1;
+    if (tau + 1 < n_tiles) issue(tau + 1, buf ^ 1);
+    const int g = tau / n_t;
+    const int q0 = (t_lo + tau - g * n_t) * kTile;
+    // skip the tile when no (query, key) pair of this wavefront is visible
+    const bool any = kw0 < N && q0 < N && !(p.causal && q0 + kTile - 1 < kw0) && !(wl >= 0 && q0 > wk_last + wl);
+    if (any) {
+      const bool need_mask = q0 + kTile > N || kw0 + kRows > N || (p.causal && q0 < kw0 + kRows - 1) ||
+                             (wl >= 0 && q0 + kTile - 1 > kw0 + wl);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x16 s = rows_times_own<E, D>(sQ[buf], h, l32, hh, kf);    // S[query][key]
+        const f32x16 dp = rows_times_own<E, D>(sO[buf], h, l32, hh, vf);   // dP[query][key]
+        float pv[16], dsv[16];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int r = 32 * h + 8 * m + 4 * hh;  // tile row of elements 4m .. 4m+3
+          const float4 l2 = *(const float4*)(&sL[buf][r]);
+          const float4 dd = *(const float4*)(&sD[buf][r]);
+          const float l2v[4] = {l2.x, l2.y, l2.z, l2.w};
+          const float ddv[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * m + e;
+            float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.scale_log2, -l2v[e]));
+            float de = pe * (dp[i] - ddv[e]);
+            if (need_mask) {
+              const bool vis = (unsigned)(q0 + r + e - vq_lo) <= vq_span;
+              pe = vis ? pe : 0.f;
+              de = vis ? de : 0.f;
+            }
+            pv[i] = pe;
+            dsv[i] = de;
+          }
+        }
+        u32x4 pf[2], df[2];
+        pack_operands<E>(pv, pf);
+        pack_operands<E>(dsv, df);
+#pragma unroll
+        for (int ct = 0; ct < S::kOutTiles; ++ct) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            dv[ct] = E::mma(tr_operand<D>(sO[buf], 2 * h + j, ct, row_lane, col_lane), pf[j], dv[ct]);
+            dk[ct] = E::mma(tr_operand<D>(sQ[buf], 2 * h + j, ct, row_lane, col_lane), df[j], dk[ct]);
+          }
+        }
+      }
+    }
+    barrier_all();
+  }
+  if (myk < N) {
+    store_row<E, D>((unsigned short*)p.dk + kv_head + (long long)myk * D, dk, p.scale, hh);
+    store_row<E, D>((unsigned short*)p.dv + kv_head + (long long)myk * D, dv, 1.f, hh);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ: workgroup = (batch, query head, 128 queries), as in the forward.
+
+template <typename E, int D>
+__global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p) {
+  using S = Shape<D>;
+  __shared__ __attribute__((aligned(16))) unsigned short sK[2][kTile * D];
+  __shared__ __attribute__((aligned(16))) unsigned short sV[2][kTile * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWaveSize - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWaveSize);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int g16 = lane >> 4, gi = lane & 15;
+  const int row_lane = 4 * hh + (gi >> 2), col_lane = 16 * (g16 & 1) + 4 * (gi & 3);
+
+  // work item: the forward's order (causal: last query block first)
+  const int L = xcd_slice_index(blockIdx.x, p.items_dq);
+  const int per_group = p.group * p.n_blocks;
+  const int gidx = L / per_group;
+  const int w = L - gidx * per_group;
+  const int qrank = w / p.group;
+  const int hg = w - qrank * p.group;
+  const int b = gidx / p.Hkv;
+  const int hk = gidx - b * p.Hkv;
+  const long long bh = (long long)b * p.Hq + hk * p.group + hg;
+  const int qb = p.causal ? (p.n_blocks - 1 - qrank) : qrank;
+  const int N = p.N;
+  const int q0 = qb * kBlock;
+  const int wq0 = q0 + wave * kRows;
+  const int myq = wq0 + l32;
+  const long long q_head = bh * N * D;
+  const long long kv_head = ((long long)b * p.Hkv + hk) * N * D;
+
+  u32x4 qf[S::kSteps], of[S::kSteps];
+  load_own_row<D>((const unsigned short*)p.q + q_head + (long long)myq * D, myq < N, hh, qf);
+  load_own_row<D>((const unsigned short*)p.dout + q_head + (long long)myq * D, myq < N, hh, of);
+  const float l2 = myq < N ? p.lse2[bh * N + myq] : INFINITY;  // rows past the end: P = 0
+  const float dd = myq < N ? p.delta[bh * N + myq] : 0.f;
+  f32x16 dq[S::kOutTiles];
+#pragma unroll
+  for (int ct = 0; ct < S::kOutTiles; ++ct) dq[ct] = f32x16{};
+
+  // key tiles this workgroup needs, and this lane's visible keys
+  const int wl = p.window_left;
+  const int kend = p.causal ? min(N, q0 + kBlock) : N;
+  const int kbeg = wl >= 0 ? max(0, q0 - wl) : 0;
+  const int t_beg = kbeg / kTile, t_end = (kend + kTile - 1) / kTile;
+  const int vis_lo = wl >= 0 ? max(0, myq - wl) : 0;
+  const unsigned vis_span = (unsigned)((p.causal ? min(myq, N - 1) : N - 1) - vis_lo);
+  const int wq1 = min(N, wq0 + kRows) - 1;
+
+  CopyOffsets<D> co;
+  co.init(wave, lane);
+  const int head_bytes = N * S::kRowBytes;
+  auto issue = [&](int t, int buf) {
+    copy_tile<D>(head_rsrc(p.k, 2 * kv_head, head_bytes), co, sK[buf], t * kTile, wave);
+    copy_tile<D>(head_rsrc(p.v, 2 * kv_head, head_bytes), co, sV[buf], t * kTile, wave);
+  };
+
+  if (t_beg < t_end) issue(t_beg, 0);
+  barrier_all();
+  for (int t = t_beg; t < t_end; ++t) {
+    const int buf = (t - t_beg) & 1;
+    if (t + 1 < t_end) issue(t + 1, buf ^ 1);
+    const int kb = t * kTile;
+    const bool any = wq0 < N && !(p.causal && kb > wq1) && !(wl >= 0 && kb + kTile - 1 < wq0 - wl);
+    if (any) {
+      const bool need_mask = kb + kTile > N || (p.causal && kb + kTile - 1 > wq0) || (wl >= 0 && kb < wq1 - wl);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x16 s = rows_times_own<E, D>(sK[buf], h, l32, hh, qf);   // S^T[key][query]
+        const f32x16 dp = rows_times_own<E, D>(sV[buf], h, l32, hh, of);  // dP^T[key][query]
+        float dsv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.scale_log2, -l2));
+          float de = pe * (dp[i] - dd);
+          if (need_mask) {
+            const int key = kb + 32 * h + 8 * (i >> 2) + 4 * hh + (i & 3);
+            de = (unsigned)(key - vis_lo) <= vis_span ? de : 0.f;
+          }
+          dsv[i] = de;
+        }
+        u32x4 df[2];
+        pack_operands<E>(dsv, df);
+#pragma unroll
+        for (int ct = 0; ct < S::kOutTiles; ++ct) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            dq[ct] = E::mma(tr_operand<D>(sK[buf], 2 * h + j, ct, row_lane, col_lane), df[j], dq[ct]);
+        }
+      }
+    }
+    barrier_all();
+  }
+  if (myq < N) store_row<E, D>((unsigned short*)p.dq + q_head + (long long)myq * D, dq, p.scale, hh);
+}
+
+template <typename E, int D>
+hipError_t launch(const BwdArgs& a, hipStream_t stream) {
+  const BwdParams p = make_bwd_params(a, kBlock);
+  constexpr int kRowsPerPrepBlock = 256 / (D / 8);
+  const long long prep_blocks = (p.rows + kRowsPerPrepBlock - 1) / kRowsPerPrepBlock;
+  hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)prep_blocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D>), dim3(p.items_dkv), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D>), dim3(p.items_dq), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+  return a.d == 64 ? launch<Bf16, 64>(a, stream) : launch<Bf16, 128>(a, stream);
+}
+
+hipError_t launch_bwd_f16(const BwdArgs& a, hipStream_t stream) {
+  return a.d == 64 ? launch<F16, 64>(a, stream) : launch<F16, 128>(a, stream);
+}
+
+long long bwd_rows_per_workgroup() { return kBlock; }
+
+}  // namespace fa

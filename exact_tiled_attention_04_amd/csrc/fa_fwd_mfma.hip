@@ -41,22 +41,15 @@
 // row max and row sum need one exchange between the two half-waves
 // (v_permlane32_swap) and the rescale and 1/l are per-lane scalars.
 #include "fa_internal.h"
+#include "fa_mfma_common.h"
 
 #include <type_traits>
 
 namespace fa {
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+using namespace mfma;
 
-constexpr int kWaveSize = 64;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaveSize * kWaves;
 constexpr int kRowsPerWave = 32;
@@ -78,29 +71,6 @@ constexpr int kWavesPerSimd = FA_WAVES_PER_SIMD;
 static_assert(kBC == 32 || kBC == 64, "tile width");
 static_assert(kVBufs == 2 || kVBufs == 3, "V buffering");
 constexpr float kLn2 = 0.69314718055994531f;
-
-struct Bf16 {
-  static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-  // two floats -> two bf16 (round to nearest even) in one dword, low first
-  static __device__ __forceinline__ unsigned pack2(float lo, float hi) {
-    bf16x2 v = {(__bf16)lo, (__bf16)hi};
-    return __builtin_bit_cast(unsigned, v);
-  }
-};
-
-struct F16 {
-  static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ unsigned pack2(float lo, float hi) {
-    f16x2 v = {(_Float16)lo, (_Float16)hi};
-    return __builtin_bit_cast(unsigned, v);
-  }
-};
 
 template <int D>
 struct Shape {
@@ -141,21 +111,6 @@ __device__ __forceinline__ int v_off(int row, int col) {
   return row * D + (((col >> 3) ^ v_swz<D>(row)) << 3) + (col & 7);
 }
 
-// Exchange with the lane 32 away: returns the pair in a fixed order (lower
-// half-wave's value first) so both lanes compute bit-identical results.
-__device__ __forceinline__ void half_pair(float x, float& lo, float& hi) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  lo = __uint_as_float(r[0]);
-  hi = __uint_as_float(r[1]);
-}
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ s16x4 lds_read_tr(const unsigned short* base, int off) {
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
-}
-
 // Per-lane byte offsets (within one tile) of this lane's pieces of the
 // direct-to-LDS copies.  Each wave moves kLoadsPerWave 1-KiB pieces of each
 // tensor per tile: lane l fills LDS bytes 16l..16l+15 of its piece, so it
@@ -194,7 +149,6 @@ __device__ __forceinline__ void copy_tile_async(__amdgpu_buffer_rsrc_t r, const 
   }
 }
 
-constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 
 // PV MFMAs by which the transposing V reads run ahead of their MFMA.
 constexpr int kPvReadLead = 4;

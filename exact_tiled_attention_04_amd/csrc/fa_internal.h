@@ -49,13 +49,19 @@ struct WorkItem {
   int qb;  // query block index
 };
 
-__device__ __forceinline__ WorkItem decode_work_item(const FwdParams& p, int id) {
+// Position of workgroup `id` in the logical order: the 8 XCDs take
+// contiguous slices of it.
+__device__ __forceinline__ int xcd_slice_index(int id, int total_items) {
   constexpr int NXCD = 8;
   const int xcd = id % NXCD;
   const int r = id / NXCD;
-  const int per = p.total_items / NXCD;
-  const int rem = p.total_items % NXCD;
-  const int L = xcd * per + (xcd < rem ? xcd : rem) + r;
+  const int per = total_items / NXCD;
+  const int rem = total_items % NXCD;
+  return xcd * per + (xcd < rem ? xcd : rem) + r;
+}
+
+__device__ __forceinline__ WorkItem decode_work_item(const FwdParams& p, int id) {
+  const int L = xcd_slice_index(id, p.total_items);
   const int per_group = p.group * p.n_qblocks;
   const int gidx = L / per_group;
   const int w = L - gidx * per_group;
@@ -89,6 +95,81 @@ inline FwdParams make_params(const FwdArgs& a, int rows_per_wg) {
   p.scale_log2 = a.scale * 1.4426950408889634f;
   return p;
 }
+
+// Validated arguments of one backward call.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* work;  // 2 * B * Hq * N floats: row terms D_i, then lse_i * log2(e)
+  int B, Hq, Hkv, N, d;
+  int causal;
+  int window_left;
+  float scale;
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // [B][Hq][N]: sum_c dout * o
+  float* lse2;   // [B][Hq][N]: lse * log2(e)
+  long long rows;  // B * Hq * N
+  int B, Hq, Hkv, N;
+  int group;
+  int causal;
+  int window_left;   // -1 = none (normalised: >= N-1 becomes -1)
+  int n_blocks;      // ceil(N / 128): query blocks (dQ) or key blocks (dK/dV)
+  int items_dq;      // B * Hq * n_blocks
+  int items_dkv;     // B * Hkv * n_blocks
+  float scale;
+  float scale_log2;
+};
+
+inline BwdParams make_bwd_params(const BwdArgs& a, int rows_per_wg) {
+  BwdParams p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.dout = a.dout;
+  p.dq = a.dq;
+  p.dk = a.dk;
+  p.dv = a.dv;
+  p.rows = (long long)a.B * a.Hq * a.N;
+  p.delta = a.work;
+  p.lse2 = a.work + p.rows;
+  p.B = a.B;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.N = a.N;
+  p.group = a.Hq / a.Hkv;
+  p.causal = a.causal ? 1 : 0;
+  p.window_left = (a.window_left >= a.N - 1) ? -1 : a.window_left;
+  p.n_blocks = (a.N + rows_per_wg - 1) / rows_per_wg;
+  p.items_dq = a.B * a.Hq * p.n_blocks;
+  p.items_dkv = a.B * a.Hkv * p.n_blocks;
+  p.scale = a.scale;
+  p.scale_log2 = a.scale * 1.4426950408889634f;
+  return p;
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_f16(const BwdArgs& a, hipStream_t stream);
+long long bwd_rows_per_workgroup();
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t stream);

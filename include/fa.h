@@ -1,5 +1,5 @@
 /*
- * fa.h -- exact attention forward for AMD MI355X (gfx950), C ABI.
+ * fa.h -- exact attention forward and backward for AMD MI355X (gfx950), C ABI.
  *
  * Operation (one call):  for every batch b, query head h and query row i,
  *
@@ -47,6 +47,8 @@
  */
 #ifndef FA_H_
 #define FA_H_
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -103,6 +105,56 @@ int fa_fwd_f16(const void *q, const void *k, const void *v, void *o, float *lse,
 int fa_fwd_f32(const void *q, const void *k, const void *v, void *o, float *lse,
                int B, int Hq, int Hkv, int N, int d, int causal, int window_left,
                float scale, void *stream);
+
+/*
+ * Gradients of fa_fwd's output with respect to q, k and v.
+ *
+ * For an upstream gradient dout = dL/do (the logsumexp output is taken to
+ * carry no gradient), with P the forward's probabilities (masked pairs 0):
+ *
+ *     dv[b][g]    = sum over the query heads h of group g of  P^T dout[b][h]
+ *     dP          = dout V^T
+ *     dS          = P * (dP - D),   D_i = sum_c dout_ic * o_ic
+ *     dq[b][h]    = scale * dS K
+ *     dk[b][g]    = sum over the query heads h of group g of  scale * dS^T q[b][h]
+ *
+ * This is the derivative of the operation above (the pages give no backward
+ * formulas).  P is recomputed from q, k and the saved lse instead of being
+ * stored, the trade of extra FLOPs for less memory traffic that the Flash
+ * Attention page (heepie.pages.dev, tiling section) describes.
+ *
+ *   q, k, v      the forward's inputs (device), layouts above.
+ *   o, lse       the forward's outputs for these inputs (lse is required).
+ *   dout         upstream gradient, same element type and layout as o.
+ *   dq, dk, dv   outputs (device), element type of q, layouts of q, k, v.
+ *   workspace    device memory of fa_bwd_workspace_size(B, Hq, N) bytes,
+ *                16-byte aligned, owned by the caller; its contents on entry
+ *                are ignored and on return are unspecified.
+ *   B ... stream as for fa_fwd.  dtype: FA_DTYPE_BF16 or FA_DTYPE_F16
+ *                (FA_DTYPE_F32 returns FA_ERR_UNSUPPORTED).
+ *
+ * dq, dk, dv and the workspace must not overlap each other or any input.
+ * The library allocates nothing; the call is asynchronous on `stream` (three
+ * kernel launches) and bit-reproducible (no atomics: each key/value head's
+ * dk and dv are summed over its query heads inside one workgroup).  Errors
+ * are reported as for fa_fwd; nothing is written on failure.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+           const void *dout, void *dq, void *dk, void *dv, float *workspace,
+           int B, int Hq, int Hkv, int N, int d, int causal, int window_left,
+           float scale, void *stream, fa_dtype_t dtype);
+int fa_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                const void *dout, void *dq, void *dk, void *dv, float *workspace,
+                int B, int Hq, int Hkv, int N, int d, int causal, int window_left,
+                float scale, void *stream);
+int fa_bwd_f16(const void *q, const void *k, const void *v, const void *o, const float *lse,
+               const void *dout, void *dq, void *dk, void *dv, float *workspace,
+               int B, int Hq, int Hkv, int N, int d, int causal, int window_left,
+               float scale, void *stream);
+
+/* Bytes of workspace fa_bwd needs: 2 * B * Hq * N * sizeof(float) (0 when
+ * any size is 0 or negative). */
+size_t fa_bwd_workspace_size(int B, int Hq, int N);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *fa_status_string(int status);

@@ -28,7 +28,8 @@ the plainest reading of "the gradient of exact attention".
 
 Optionally the function also returns, for error bounds in tests, the same
 products taken over absolute values (|P|^T |dO|, scale |dS| |K|,
-scale |dS|^T |Q|) and the row terms F_i = sum_c |do_ic| |o_ic| with their
+scale |dS|^T |Q|) and the row terms F_i = sum_c |do_ic| (P |V|)_ic -- a bound
+on sum_c |do_ic| |o_ic| that also covers a rounded P inside o -- with their
 products scale (P * F) |K| and scale (P * F)^T |Q|.
 """
 from __future__ import annotations
@@ -79,8 +80,7 @@ def _one_kv_head(qs, kh, vh, dos, causal, window_left, scale, bounds):
                 mag["dv"] += P.T @ np.abs(doh[r])
                 mag["dq"][g, r] = scale * (A @ np.abs(kh))
                 mag["dk"] += scale * (A.T @ np.abs(qh[r]))
-                O = P @ vh
-                F = (np.abs(doh[r]) * np.abs(O)).sum(axis=1, keepdims=True)
+                F = (np.abs(doh[r]) * (P @ np.abs(vh))).sum(axis=1, keepdims=True)
                 PF = P * F
                 mag["dq_f"][g, r] = scale * (PF @ np.abs(kh))
                 mag["dk_f"] += scale * (PF.T @ np.abs(qh[r]))

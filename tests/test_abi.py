@@ -106,3 +106,59 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load()
+
+
+# backward: fake addresses again; every case fails (or no-ops) before a launch
+DO, DQ, DK, DV, W = 0x600000, 0x700000, 0x800000, 0x900000, 0xA00000
+GOOD_BWD = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, work=W, B=1, Hq=4, Hkv=2, N=16, d=64,
+                causal=0, window_left=-1, scale=0.125, stream=None)
+
+
+def call_bwd(dtype=_lib.FA_DTYPE_BF16, **over):
+    a = dict(GOOD_BWD, **over)
+    return _lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"], a["work"],
+                       a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"], a["window_left"], a["scale"],
+                       a["stream"], dtype)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(B=-1), _lib.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), _lib.FA_ERR_INVALID_ARG),
+    (dict(window_left=-2), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), _lib.FA_ERR_UNSUPPORTED),
+    (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
+    (dict(lse=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(dout=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(work=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(dq=DQ + 8), _lib.FA_ERR_MISALIGNED),
+    (dict(work=W + 4), _lib.FA_ERR_MISALIGNED),
+    (dict(lse=L + 2), _lib.FA_ERR_MISALIGNED),
+    (dict(dq=Q), _lib.FA_ERR_INVALID_ARG),            # output aliases an input
+    (dict(dk=DO + 64), _lib.FA_ERR_INVALID_ARG),      # output inside dout
+    (dict(dv=DK), _lib.FA_ERR_INVALID_ARG),           # two outputs alias
+    (dict(work=DV + 128), _lib.FA_ERR_INVALID_ARG),   # workspace inside dv
+])
+def test_bwd_validation_rejects(over, status):
+    assert call_bwd(**over) == status
+    assert _lib.fa_last_error() != ""
+
+
+def test_bwd_rejects_f32_and_unknown_dtype():
+    assert call_bwd(dtype=_lib.FA_DTYPE_F32) == _lib.FA_ERR_UNSUPPORTED
+    assert call_bwd(dtype=9) == _lib.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("over", [dict(B=0), dict(N=0), dict(Hq=0, q=0, work=0)])
+def test_bwd_empty_problem_is_a_noop(over):
+    assert call_bwd(**over) == _lib.FA_OK
+    assert _lib.fa_last_error() == ""
+
+
+def test_bwd_typed_entry_points_and_workspace_size():
+    for fn in (_lib.fa_bwd_bf16, _lib.fa_bwd_f16):
+        assert fn(Q, K, V, O, L, DO, DQ, DK, DV, W, 1, 4, 3, 16, 64, 0, -1, 0.1, None) == _lib.FA_ERR_INVALID_ARG
+        assert fn(Q, K, V, O, L, DO, DQ, DK, DV, W, 1, 4, 2, 16, 80, 0, -1, 0.1, None) == _lib.FA_ERR_UNSUPPORTED
+    assert _lib.fa_bwd_workspace_size(2, 16, 8192) == 2 * 2 * 16 * 8192 * 4
+    assert _lib.fa_bwd_workspace_size(0, 16, 8192) == 0
+    assert _lib.fa_bwd_workspace_size(1, -1, 10) == 0

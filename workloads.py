@@ -132,6 +132,32 @@ def random_inputs(seed: int, dtype: str, B: int, Hq: int, Hkv: int, N: int, d: i
     return make_inputs(w)
 
 
+def make_grad(w: Workload, *, N: Optional[int] = None, B: Optional[int] = None,
+              Hq: Optional[int] = None, d: Optional[int] = None):
+    """Upstream gradient dO for the backward of workload ``w``: standard normal
+    draws from the generator seeded with ``w.seed + 1000``, shaped like q,
+    exact in ``w.dtype``."""
+    B = w.B if B is None else B
+    Hq = w.Hq if Hq is None else Hq
+    N = w.N if N is None else N
+    d = w.d if d is None else d
+    rng = np.random.default_rng(w.seed + 1000)
+    return round_to(w.dtype, rng.standard_normal((B, Hq, N, d), dtype=np.float32))
+
+
+def random_grad(seed: int, dtype: str, B: int, Hq: int, N: int, d: int):
+    """Ad-hoc upstream gradient, same recipe as ``make_grad``."""
+    w = Workload("adhoc", dtype, B, Hq, Hq, N, d, False, -1, seed)
+    return make_grad(w)
+
+
+def bwd_metric_flops(w: Workload) -> float:
+    """Algorithmic FLOPs of one backward pass: five products of the forward's
+    size per visible pair (recompute S, dV, dP, dQ, dK), i.e. 2.5 x the
+    forward's metric FLOPs."""
+    return 2.5 * metric_flops(w)
+
+
 def unmasked_pairs(N: int, causal: bool, window_left: int) -> int:
     """Number of (query i, key j) pairs that a causal and/or left-window mask
     keeps, per head: key j is kept when j <= i (if causal) and j >= i - wl
