@@ -2,7 +2,7 @@
 bf16/fp16 matrix-core peak.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload causal_8k]
-                    [--no-cpu-baseline] [--all] [--copy-calibration MiB]
+                    [--no-cpu-baseline] [--all] [--copy-calibration MiB] [--bwd]
 
 One step = one forward call (the whole path: Q/K/V tile staging, both
 contractions, online softmax, epilogue) over seeded synthetic inputs already
@@ -11,6 +11,10 @@ workload, without the CPU baseline).
 
 FLOPs credited per call: 4*d per visible (query, key) pair per head; causal
 counts N^2/2 pairs, a window counts the exact visible pairs.
+
+``--bwd`` times the backward instead (one step = one ``fa.bwd`` call: the
+row-term prep, dK/dV and dQ kernels) from the forward's o and lse, credited
+2.5x the forward's FLOPs (five products of the forward's size).
 """
 from __future__ import annotations
 
@@ -26,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense MFMA (fp32: vector/matrix)
 KERNEL_NAME = {"bf16": "fwd_mfma_kernel", "f16": "fwd_mfma_kernel", "f32": "fwd_f32_kernel"}
+BWD_KERNELS = "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel"
 
 
 def kernel_source_hash() -> str:
@@ -81,6 +86,109 @@ def cpu_baseline(w, q, k, v, budget_s: float = 12.0):
     return {"value": round(value, 6), "unit": "TFLOP/s", "cores": min(cores, len(heads)), "kind": "oracle",
             "sample": f"{done} of {len(heads)} (batch, head) slices, all {w.N} query rows each, "
                       f"fp64 numpy, {dt:.1f} s wall"}
+
+
+def cpu_baseline_bwd(w, q, k, v, do, budget_s: float = 12.0):
+    """The fp64 gradient oracle, as it stands, on a bounded sample: whole
+    (batch, key/value head) groups, as many at a time as there are host cores
+    (BLAS held to one thread each), until ``budget_s`` of wall time has
+    passed."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import workloads as W
+    from oracle import attention_bwd
+
+    cores = len(os.sched_getaffinity(0))
+    g = w.Hq // w.Hkv
+    flops_per_group = W.bwd_metric_flops(w) / (w.B * w.Hkv)
+    groups = [(b, hk) for b in range(w.B) for hk in range(w.Hkv)]
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while done < len(groups) and time.perf_counter() - t0 < budget_s:
+            chunk = groups[done:done + cores]
+            qs = np.concatenate([q[b:b + 1, hk * g:(hk + 1) * g] for b, hk in chunk], axis=1)
+            dos = np.concatenate([do[b:b + 1, hk * g:(hk + 1) * g] for b, hk in chunk], axis=1)
+            ks = np.concatenate([k[b:b + 1, hk:hk + 1] for b, hk in chunk], axis=1)
+            vs = np.concatenate([v[b:b + 1, hk:hk + 1] for b, hk in chunk], axis=1)
+            attention_bwd(qs, ks, vs, dos, w.causal, w.window_left, w.scale, threads=cores)
+            done += len(chunk)
+    dt = time.perf_counter() - t0
+    return {"value": round(flops_per_group * done / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": min(cores, len(groups)), "kind": "oracle",
+            "sample": f"{done} of {len(groups)} (batch, key/value head) groups, all {w.N} rows each, "
+                      f"fp64 numpy, {dt:.1f} s wall"}
+
+
+def run_bwd(args, name, with_cpu):
+    import numpy as np
+    import torch
+
+    import exact_tiled_attention_04_amd as fa
+    import workloads as W
+
+    w = W.WORKLOADS[name]
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    q, k, v = W.make_inputs(w)
+    do = W.make_grad(w)
+    qd, kd, vd, dod = (torch.from_numpy(x).to(tdt).cuda() for x in (q, k, v, do))
+    o, lse = fa.fwd(qd, kd, vd, causal=w.causal, window_left=w.window_left, scale=w.scale)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    ws = torch.empty(fa._lib.fa_bwd_workspace_size(w.B, w.Hq, w.N) // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, window_left=w.window_left, scale=w.scale,
+               dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream)
+
+    print(f"[bench] {name} bwd: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    print(f"[bench] {name} bwd: timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
+    avg_ms = float(np.mean(per_call_ms))
+    flops = W.bwd_metric_flops(w)
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    rec = {
+        "metric": "attention bwd TFLOP/s + % of MI355X bf16 MFMA peak (2.5x forward FLOPs)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "config": {"workload": name + " (backward)", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "window_left": w.window_left, "scale": w.scale,
+                   "seed": w.seed, "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": BWD_KERNELS,
+                     "avg_call_us": round(avg_ms * 1e3, 2),
+                     "min_call_us": round(float(np.min(per_call_ms)) * 1e3, 2)},
+    }
+    if with_cpu:
+        print(f"[bench] {name} bwd: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, do)
+    return rec
 
 
 def run(args, name, with_cpu):
@@ -178,6 +286,7 @@ def main():
     ap.add_argument("--all", action="store_true", help="one line per workload (no CPU baseline)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="also run a device copy of this size (counter calibration)")
+    ap.add_argument("--bwd", action="store_true", help="time the backward pass instead of the forward")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the forward kernel runs on a single device "
@@ -188,8 +297,13 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    import workloads as W
+    if args.bwd:
+        names = [n for n in W.ORDER if W.WORKLOADS[n].dtype != "f32"] if args.all else [args.workload]
+        for name in names:
+            print(json.dumps(run_bwd(args, name, not args.all and not args.no_cpu_baseline)), flush=True)
+        return
     if args.all:
-        import workloads as W
         for name in W.ORDER:
             print(json.dumps(run(args, name, False)), flush=True)
         return

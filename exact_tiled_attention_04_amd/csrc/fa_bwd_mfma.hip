@@ -54,15 +54,15 @@ constexpr int kBlock = kWaves * kRows;   // rows a workgroup owns
 constexpr int kTile = 64;                // streamed rows per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int D>
+template <int D, int W = kWaves>
 struct Shape {
   static constexpr int kChunks = D / 8;     // 16-byte chunks per row
   static constexpr int kSteps = D / 16;     // MFMA k-steps over the head dimension
   static constexpr int kOutTiles = D / 32;  // 32-wide output tiles over the head dimension
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows per 1-KiB wave-wide load
-  static constexpr int kLoadsPerWave = kTile / kRowsPerLoad / kWaves;
-  static_assert(kTile % (kRowsPerLoad * kWaves) == 0, "tile must split evenly over the wavefronts");
+  static constexpr int kLoadsPerWave = kTile / kRowsPerLoad / W;  // copy share of each of W wavefronts
+  static_assert(kTile % (kRowsPerLoad * W) == 0, "tile must split evenly over the wavefronts");
 };
 
 // Chunk swizzle of a streamed tile.  Row reads: 16 lanes on 16 consecutive
@@ -88,11 +88,11 @@ __device__ __forceinline__ int tr_off(int row, int col) {  // element offset of 
 // Per-lane source offsets of this lane's part of a tile copy: lane l fills
 // LDS bytes 16l..16l+15 of its 1-KiB piece, i.e. physical chunk l % kChunks
 // of its row, so it fetches the logical chunk the swizzle maps there.
-template <int D>
+template <int D, int W = kWaves>
 struct CopyOffsets {
-  int off[Shape<D>::kLoadsPerWave];
+  int off[Shape<D, W>::kLoadsPerWave];
   __device__ __forceinline__ void init(int wave, int lane) {
-    using S = Shape<D>;
+    using S = Shape<D, W>;
 #pragma unroll
     for (int u = 0; u < S::kLoadsPerWave; ++u) {
       const int piece = wave * S::kLoadsPerWave + u;
@@ -105,10 +105,10 @@ struct CopyOffsets {
 
 // Copy rows row0 .. row0+kTile-1 of the tensor behind `r` (bounded to the
 // head's N rows: rows past the end arrive as zeros) straight into LDS.
-template <int D>
-__device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t r, const CopyOffsets<D>& c,
+template <int D, int W = kWaves>
+__device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t r, const CopyOffsets<D, W>& c,
                                           unsigned short* dst, int row0, int wave) {
-  using S = Shape<D>;
+  using S = Shape<D, W>;
   // (builtin arguments go through plain ints: the host compilation pass
   // rejects template-dependent expressions in this builtin's operands)
   const int soff = row0 * S::kRowBytes;
@@ -155,6 +155,21 @@ __device__ __forceinline__ f32x16 rows_times_own(const unsigned short* __restric
   for (int kc = 0; kc < Shape<D>::kSteps; ++kc) {
     const u32x4 a = *(const u32x4*)(t + row_off<D>(32 * h + l32, 2 * kc + hh));
     acc = E::mma(a, own[kc], acc);
+  }
+  return acc;
+}
+
+// The same product with the wavefront's own rows read from LDS as B operands
+// (own rows own_row0 .. own_row0+31 of `own`, stored like a streamed tile).
+template <typename E, int D>
+__device__ __forceinline__ f32x16 rows_times_lds(const unsigned short* __restrict__ t, int h, int l32, int hh,
+                                                 const unsigned short* __restrict__ own, int own_row0) {
+  f32x16 acc = f32x16{};
+#pragma unroll
+  for (int kc = 0; kc < Shape<D>::kSteps; ++kc) {
+    const u32x4 a = *(const u32x4*)(t + row_off<D>(32 * h + l32, 2 * kc + hh));
+    const u32x4 b = *(const u32x4*)(own + row_off<D>(own_row0 + l32, 2 * kc + hh));
+    acc = E::mma(a, b, acc);
   }
   return acc;
 }
@@ -243,19 +258,40 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 2. dK, dV: workgroup = (batch, key/value head, 128 keys).
+// 2. dK, dV: workgroup = (batch, key/value head, 128 keys), 8 wavefronts.
+//
+// Wavefronts w and w+4 own the same 32 keys (group w % 4) and take opposite
+// 32-query halves of every 64-row query tile, so the two share a SIMD and
+// hide each other's latencies without repeating any product.  Each keeps
+// partial dK^T, dV^T for its keys; the halves are summed through LDS once at
+// the end.
+
+constexpr int kDkvWaves = 8;
+constexpr int kDkvThreads = kWaveSize * kDkvWaves;
+
+// At D = 128 the V rows of the workgroup's keys are read from LDS as MFMA
+// operands instead of living in registers (32 VGPRs a lane): with two
+// wavefronts per SIMD each has 256 registers in all.
+template <int D>
+constexpr bool kVInLds = D == 128;
 
 template <typename E, int D>
-__global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p) {
-  using S = Shape<D>;
-  __shared__ __attribute__((aligned(16))) unsigned short sQ[2][kTile * D];
-  __shared__ __attribute__((aligned(16))) unsigned short sO[2][kTile * D];  // dO tiles
+__global__ void __launch_bounds__(kDkvThreads) bwd_dkdv_kernel(BwdParams p) {
+  using S = Shape<D, kDkvWaves>;
+  // Q and dO tiles (double-buffered) in one array: at the end its space holds
+  // the partial sums exchanged between the two query halves
+  __shared__ __attribute__((aligned(16))) unsigned short sT[2][2][kTile * D];
+  unsigned short(*sQ)[kTile * D] = sT[0];
+  unsigned short(*sO)[kTile * D] = sT[1];  // dO tiles
   __shared__ __attribute__((aligned(16))) float sL[2][kTile];               // lse * log2(e)
   __shared__ __attribute__((aligned(16))) float sD[2][kTile];               // D
+  __shared__ __attribute__((aligned(16))) unsigned short sVk[kVInLds<D> ? kBlock * D : 8];  // V rows of the block
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWaveSize - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWaveSize);
+  const int kg = wave & 3;   // key group
+  const int qh = wave >> 2;  // query half of each tile
   const int l32 = lane & 31, hh = lane >> 5;
   const int g16 = lane >> 4, gi = lane & 15;
   const int row_lane = 4 * hh + (gi >> 2), col_lane = 16 * (g16 & 1) + 4 * (gi & 3);
@@ -268,13 +304,13 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p) {
   const int hk = bk - b * p.Hkv;
   const int N = p.N;
   const int k0 = kb * kBlock;
-  const int kw0 = k0 + wave * kRows;
+  const int kw0 = k0 + kg * kRows;
   const int myk = kw0 + l32;
   const long long kv_head = ((long long)b * p.Hkv + hk) * N * D;
 
-  u32x4 kf[S::kSteps], vf[S::kSteps];
+  u32x4 kf[S::kSteps], vf[kVInLds<D> ? 1 : S::kSteps];
   load_own_row<D>((const unsigned short*)p.k + kv_head + (long long)myk * D, myk < N, hh, kf);
-  load_own_row<D>((const unsigned short*)p.v + kv_head + (long long)myk * D, myk < N, hh, vf);
+  if (!kVInLds<D>) load_own_row<D>((const unsigned short*)p.v + kv_head + (long long)myk * D, myk < N, hh, vf);
   f32x16 dk[S::kOutTiles], dv[S::kOutTiles];
 #pragma unroll
   for (int ct = 0; ct < S::kOutTiles; ++ct) dk[ct] = dv[ct] = f32x16{};
@@ -294,73 +330,115 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p) {
   const unsigned vq_span = myk < N ? (unsigned)((wl >= 0 ? min(N - 1, myk + wl) : N - 1) - vq_lo) : 0u;
   const int wk_last = min(N - 1, kw0 + kRows - 1);
 
-  CopyOffsets<D> co;
+  CopyOffsets<D, kDkvWaves> co;
   co.init(wave, lane);
   const int head_bytes = N * S::kRowBytes;
   auto issue = [&](int tau, int buf) {
     const int g = tau / n_t;
     const int q0 = (t_lo + tau - g * n_t) * kTile;
     const long long bh = (long long)b * p.Hq + hk * p.group + g;
-    copy_tile<D>(head_rsrc(p.q, 2 * bh * N * D, head_bytes), co, sQ[buf], q0, wave);
-    copy_tile<D>(head_rsrc(p.dout, 2 * bh * N * D, head_bytes), co, sO[buf], q0, wave);
+    copy_tile<D, kDkvWaves>(head_rsrc(p.q, 2 * bh * N * D, head_bytes), co, sQ[buf], q0, wave);
+    copy_tile<D, kDkvWaves>(head_rsrc(p.dout, 2 * bh * N * D, head_bytes), co, sO[buf], q0, wave);
     if (wave == 0) copy_vec(head_rsrc(p.lse2, 4 * bh * N, 4 * N), sL[buf], q0, lane);
     if (wave == 1) copy_vec(head_rsrc(p.delta, 4 * bh * N, 4 * N), sD[buf], q0, lane);
   };
 
+  if (kVInLds<D>) {  // rows k0 .. k0+127 of V (zeros past the end)
+#pragma unroll
+    for (int part = 0; part < kBlock / kTile; ++part)
+      copy_tile<D, kDkvWaves>(head_rsrc(p.v, 2 * kv_head, head_bytes), co, sVk + part * kTile * D,
+                              k0 + part * kTile, wave);
+  }
   issue(0, 0);
   barrier_all();
+  const float c = p.scale_log2;
   for (int tau = 0; tau < n_tiles; ++tau) {
     const int buf = tau & 1;
     if (tau + 1 < n_tiles) issue(tau + 1, buf ^ 1);
     const int g = tau / n_t;
-    const int q0 = (t_lo + tau - g * n_t) * kTile;
-    // skip the tile when no (query, key) pair of this wavefront is visible
-    const bool any = kw0 < N && q0 < N && !(p.causal && q0 + kTile - 1 < kw0) && !(wl >= 0 && q0 > wk_last + wl);
+    const int qs = (t_lo + tau - g * n_t) * kTile + 32 * qh;  // first query of this wave's half
+    // skip the half when no (query, key) pair of this wavefront is visible
+    const bool any = kw0 < N && qs < N && !(p.causal && qs + 31 < kw0) && !(wl >= 0 && qs > wk_last + wl);
     if (any) {
-      const bool need_mask = q0 + kTile > N || kw0 + kRows > N || (p.causal && q0 < kw0 + kRows - 1) ||
-                             (wl >= 0 && q0 + kTile - 1 > kw0 + wl);
+      const bool need_mask = qs + 32 > N || kw0 + kRows > N || (p.causal && qs < kw0 + kRows - 1) ||
+                             (wl >= 0 && qs + 31 > kw0 + wl);
+      const f32x16 s = rows_times_own<E, D>(sQ[buf], qh, l32, hh, kf);  // S[query][key]
+      const f32x16 dp = kVInLds<D> ? rows_times_lds<E, D>(sO[buf], qh, l32, hh, sVk, kg * kRows)
+                                   : rows_times_own<E, D>(sO[buf], qh, l32, hh, vf);
+      float pv[16], dsv[16];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const f32x16 s = rows_times_own<E, D>(sQ[buf], h, l32, hh, kf);    // S[query][key]
-        const f32x16 dp = rows_times_own<E, D>(sO[buf], h, l32, hh, vf);   // dP[query][key]
-        float pv[16], dsv[16];
+      for (int m = 0; m < 4; ++m) {
+        const int r = 32 * qh + 8 * m + 4 * hh;  // tile row of elements 4m .. 4m+3
+        const float4 l2 = *(const float4*)(&sL[buf][r]);
+        const float4 dd = *(const float4*)(&sD[buf][r]);
+        const float l2v[4] = {l2.x, l2.y, l2.z, l2.w};
+        const float ddv[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int r = 32 * h + 8 * m + 4 * hh;  // tile row of elements 4m .. 4m+3
-          const float4 l2 = *(const float4*)(&sL[buf][r]);
-          const float4 dd = *(const float4*)(&sD[buf][r]);
-          const float l2v[4] = {l2.x, l2.y, l2.z, l2.w};
-          const float ddv[4] = {dd.x, dd.y, dd.z, dd.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * m + e;
-            float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.scale_log2, -l2v[e]));
-            float de = pe * (dp[i] - ddv[e]);
-            if (need_mask) {
-              const bool vis = (unsigned)(q0 + r + e - vq_lo) <= vq_span;
-              pe = vis ? pe : 0.f;
-              de = vis ? de : 0.f;
-            }
-            pv[i] = pe;
-            dsv[i] = de;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * m + e;
+          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -l2v[e]));
+          dsv[i] = pv[i] * (dp[i] - ddv[e]);
         }
-        u32x4 pf[2], df[2];
-        pack_operands<E>(pv, pf);
-        pack_operands<E>(dsv, df);
+      }
+      if (need_mask) {
+        const int r0 = qs - 32 * qh;  // tile's first query
 #pragma unroll
-        for (int ct = 0; ct < S::kOutTiles; ++ct) {
+        for (int i = 0; i < 16; ++i) {
+          const int q = r0 + 32 * qh + 8 * (i >> 2) + 4 * hh + (i & 3);
+          const bool vis = (unsigned)(q - vq_lo) <= vq_span;
+          pv[i] = vis ? pv[i] : 0.f;
+          dsv[i] = vis ? dsv[i] : 0.f;
+        }
+      }
+      u32x4 pf[2], df[2];
+      pack_operands<E>(pv, pf);
+      pack_operands<E>(dsv, df);
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            dv[ct] = E::mma(tr_operand<D>(sO[buf], 2 * h + j, ct, row_lane, col_lane), pf[j], dv[ct]);
-            dk[ct] = E::mma(tr_operand<D>(sQ[buf], 2 * h + j, ct, row_lane, col_lane), df[j], dk[ct]);
-          }
+      for (int ct = 0; ct < S::kOutTiles; ++ct) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          dv[ct] = E::mma(tr_operand<D>(sO[buf], 2 * qh + j, ct, row_lane, col_lane), pf[j], dv[ct]);
+          dk[ct] = E::mma(tr_operand<D>(sQ[buf], 2 * qh + j, ct, row_lane, col_lane), df[j], dk[ct]);
         }
       }
     }
     barrier_all();
   }
-  if (myk < N) {
+
+  // sum the two halves' partials: waves 4..7 hand theirs to waves 0..3
+  // through the (now idle) tile buffers, one tensor at a time; element
+  // 4x+y of lane l of key group kg sits at float (((kg*U + x)*64 + l)*4 + y),
+  // U = 4*kOutTiles, so 16-byte accesses of a wave hit consecutive addresses
+  constexpr int U = 4 * S::kOutTiles;
+  static_assert(sizeof(sT) >= kWaves * U * kWaveSize * 16, "partials must fit the tile buffers");
+  float* part = reinterpret_cast<float*>(&sT[0][0][0]);
+  auto exchange = [&](f32x16* acc) {
+    if (qh == 1) {
+#pragma unroll
+      for (int ct = 0; ct < S::kOutTiles; ++ct)
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          *(float4*)(part + (((kg * U + 4 * ct + x) * kWaveSize + lane) << 2)) =
+              float4{acc[ct][4 * x], acc[ct][4 * x + 1], acc[ct][4 * x + 2], acc[ct][4 * x + 3]};
+    }
+    barrier_all();
+    if (qh == 0) {
+#pragma unroll
+      for (int ct = 0; ct < S::kOutTiles; ++ct)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const float4 o = *(const float4*)(part + (((kg * U + 4 * ct + x) * kWaveSize + lane) << 2));
+          acc[ct][4 * x] += o.x;
+          acc[ct][4 * x + 1] += o.y;
+          acc[ct][4 * x + 2] += o.z;
+          acc[ct][4 * x + 3] += o.w;
+        }
+    }
+    barrier_all();
+  };
+  exchange(dk);
+  exchange(dv);
+  if (qh == 0 && myk < N) {
     store_row<E, D>((unsigned short*)p.dk + kv_head + (long long)myk * D, dk, p.scale, hh);
     store_row<E, D>((unsigned short*)p.dv + kv_head + (long long)myk * D, dv, 1.f, hh);
   }
@@ -471,7 +549,7 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   constexpr int kRowsPerPrepBlock = 256 / (D / 8);
   const long long prep_blocks = (p.rows + kRowsPerPrepBlock - 1) / kRowsPerPrepBlock;
   hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)prep_blocks), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D>), dim3(p.items_dkv), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D>), dim3(p.items_dkv), dim3(kDkvThreads), 0, stream, p);
   hipLaunchKernelGGL((bwd_dq_kernel<E, D>), dim3(p.items_dq), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
