@@ -88,6 +88,21 @@ def cpu_baseline(w, q, k, v, budget_s: float = 12.0):
                       f"fp64 numpy, {dt:.1f} s wall"}
 
 
+def calibration_copy(mib: int):
+    """A device-to-device copy of ``mib`` MiB (x3), whose counter readings
+    calibrate FETCH_SIZE / WRITE_SIZE in the same profiled run."""
+    if not mib:
+        return None
+    import torch
+    nbytes = mib * 2 ** 20
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return f"copied {nbytes} bytes x3 for counter calibration"
+
+
 def cpu_baseline_bwd(w, q, k, v, do, budget_s: float = 12.0):
     """The fp64 gradient oracle, as it stands, on a bounded sample: whole
     (batch, key/value head) groups, as many at a time as there are host cores
@@ -185,6 +200,9 @@ def run_bwd(args, name, with_cpu):
                      "avg_call_us": round(avg_ms * 1e3, 2),
                      "min_call_us": round(float(np.min(per_call_ms)) * 1e3, 2)},
     }
+    copy_note = calibration_copy(args.copy_calibration)
+    if copy_note:
+        rec["calibration"] = copy_note
     if with_cpu:
         print(f"[bench] {name} bwd: cpu baseline (oracle)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, do)
@@ -232,15 +250,7 @@ def run(args, name, with_cpu):
     achieved = flops / (avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     traffic = measured_traffic(name)
-    copy_note = None
-    if args.copy_calibration:
-        nbytes = args.copy_calibration * 2 ** 20
-        src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        copy_note = f"copied {nbytes} bytes x3 for counter calibration"
+    copy_note = calibration_copy(args.copy_calibration)
     rec = {
         "metric": "attention fwd TFLOP/s + % of MI355X bf16 MFMA peak (d=128, causal, N=8k)",
         "value": round(value, 3),

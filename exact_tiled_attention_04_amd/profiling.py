@@ -14,6 +14,9 @@ files under ``profiles/``.
 --pmc     further counter-collection directories (SQ_*/GRBM_* counters), summed
           per dispatch of the attention kernel
 --last    use only the last N dispatches of the kernel (the timed steps)
+--kernel  substring selecting the kernel (default: the forward, "fwd_")
+--name    output base name (default: fwd_<workload>; the traffic JSON that
+          bench.py reads is written only for the forward)
 """
 from __future__ import annotations
 
@@ -98,12 +101,19 @@ def main():
     ap.add_argument("--pmc", nargs="*", default=[])
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--last", type=int, default=None)
+    ap.add_argument("--kernel", default="fwd_")
+    ap.add_argument("--name", default=None)
     ap.add_argument("--flops", type=float, default=None, help="algorithmic FLOPs per launch")
     ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     args = ap.parse_args()
+    global KERNEL_KEY
+    KERNEL_KEY = args.kernel
+    forward = args.kernel == "fwd_"
+    name = args.name or f"fwd_{args.workload}"
 
     tr = trace_summary(args.trace, args.last)
-    lines = [f"# attention forward kernel, workload {args.workload}", "",
+    title = "attention forward kernel" if forward else f"attention kernel matching '{args.kernel}'"
+    lines = [f"# {title}, workload {args.workload}", "",
              "Commands (run from the repository root on one MI355X):", ""]
     lines += [f"    {c}" for c in args.command]
     lines += ["", f"kernel: `{tr['kernel']}`",
@@ -134,11 +144,12 @@ def main():
                   f"{copy_bytes // 1024} KiB -> factor {w_scale:.4f}; kernel {statistics.mean(fa_w['WRITE_SIZE']):.0f} KiB "
                   f"-> {write_b / 2**20:.1f} MiB written",
                   f"  total {traffic / 2**20:.1f} MiB per launch"]
-        json.dump({"workload": args.workload, "kernel_source_sha256": kernel_source_hash(),
-                   "hbm_bytes_per_launch": round(traffic), "fetch_bytes": round(fetch_b),
-                   "write_bytes": round(write_b), "fetch_scale": f_scale, "write_scale": w_scale,
-                   "commands": args.command},
-                  open(os.path.join(args.out_dir, f"traffic_{args.workload}.json"), "w"), indent=1)
+        if forward:
+            json.dump({"workload": args.workload, "kernel_source_sha256": kernel_source_hash(),
+                       "hbm_bytes_per_launch": round(traffic), "fetch_bytes": round(fetch_b),
+                       "write_bytes": round(write_b), "fetch_scale": f_scale, "write_scale": w_scale,
+                       "commands": args.command},
+                      open(os.path.join(args.out_dir, f"traffic_{args.workload}.json"), "w"), indent=1)
     for d in args.pmc:
         a, _ = counter_per_dispatch(d, args.last)
         lines += ["", f"counters ({os.path.basename(os.path.normpath(d))}), mean per dispatch:"]
@@ -155,7 +166,7 @@ def main():
             bc = statistics.mean(a["SQ_LDS_BANK_CONFLICT"]) / max(1.0, statistics.mean(a["SQ_LDS_IDX_ACTIVE"]))
             lines.append(f"  LDS bank-conflict cycles / LDS active cycles = {100 * bc:.2f}%")
     lines.append(f"\nkernel sources sha256 {kernel_source_hash()}")
-    out = os.path.join(args.out_dir, f"fwd_{args.workload}.md")
+    out = os.path.join(args.out_dir, f"{name}.md")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
