@@ -44,12 +44,16 @@ def masked(i: np.ndarray, j: np.ndarray, causal: bool, window_left: int) -> np.n
     return m
 
 
-def _one_head(qh, kh, vh, rows, causal, window_left, scale):
-    """Attention for one (batch, query head): returns (O rows, lse rows)."""
+def _one_head(qh, kh, vh, rows, causal, window_left, scale, tail=None):
+    """Attention for one (batch, query head): returns (O rows, lse rows) and,
+    when ``tail`` is given, the magnitude rows (P|V|, sum_j min(p_ij,
+    tail * max_j p_ij) |v_j|)."""
     N = kh.shape[0]
     d = vh.shape[1]
     out_o = np.empty((len(rows), d), dtype=np.float64)
     out_l = np.empty(len(rows), dtype=np.float64)
+    mag_pv = np.empty((len(rows), d), dtype=np.float64) if tail is not None else None
+    mag_tail = np.empty((len(rows), d), dtype=np.float64) if tail is not None else None
     keys = np.arange(N)
     for s0 in range(0, len(rows), ROW_BLOCK):
         r = rows[s0:s0 + ROW_BLOCK]
@@ -64,18 +68,29 @@ def _one_head(qh, kh, vh, rows, causal, window_left, scale):
         # phase 3: O = P V
         out_o[s0:s0 + len(r)] = P @ vh
         out_l[s0:s0 + len(r)] = m[:, 0] + np.log(z[:, 0])
+        if tail is not None:
+            mag_pv[s0:s0 + len(r)] = P @ np.abs(vh)
+            small = np.minimum(P, tail * P.max(axis=1, keepdims=True))
+            mag_tail[s0:s0 + len(r)] = small @ np.abs(vh)
+    if tail is not None:
+        return out_o, out_l, mag_pv, mag_tail
     return out_o, out_l
 
 
 def attention_fwd(q, k, v, causal: bool = False, window_left: int = -1,
                   scale: Optional[float] = None, rows: Optional[Sequence[int]] = None,
-                  threads: Optional[int] = None):
+                  threads: Optional[int] = None, tail: Optional[float] = None):
     """Exact attention forward in float64.
 
     q: [B, Hq, N, d]; k, v: [B, Hkv, N, d] (any float dtype; widened to fp64).
     rows: optional query-row indices to evaluate (same for every head); the
     default is every row.  Returns (o [B, Hq, R, d] fp64, lse [B, Hq, R] fp64)
     where R = len(rows).
+
+    With ``tail`` (a fraction), also returns a dict of magnitudes for error
+    bounds, shaped like o: 'pv' = P|V| and 'tail' = sum_j min(p_ij, tail *
+    max_j p_ij) |v_j| (the mass of probabilities below that fraction of their
+    row's largest, as if dropped, bounded by it).
 
     Raises ValueError on inconsistent shapes, Hq not a multiple of Hkv, or
     window_left < -1.  Every row has at least one visible key (key j = i is
@@ -101,8 +116,9 @@ def attention_fwd(q, k, v, causal: bool = False, window_left: int = -1,
     R = len(rows)
     o = np.empty((B, Hq, R, d), dtype=np.float64)
     lse = np.empty((B, Hq, R), dtype=np.float64)
+    mags = {"pv": np.empty_like(o), "tail": np.empty_like(o)} if tail is not None else None
     if B * Hq * R == 0:
-        return o, lse
+        return (o, lse, mags) if tail is not None else (o, lse)
 
     def work(bh):
         b, h = divmod(bh, Hq)
@@ -110,7 +126,10 @@ def attention_fwd(q, k, v, causal: bool = False, window_left: int = -1,
         qh = q[b, h].astype(np.float64)
         kh = k[b, hk].astype(np.float64)
         vh = v[b, hk].astype(np.float64)
-        o[b, h], lse[b, h] = _one_head(qh, kh, vh, rows, causal, window_left, scale)
+        res = _one_head(qh, kh, vh, rows, causal, window_left, scale, tail)
+        o[b, h], lse[b, h] = res[0], res[1]
+        if tail is not None:
+            mags["pv"][b, h], mags["tail"][b, h] = res[2], res[3]
 
     nthreads = threads or len(os.sched_getaffinity(0))
     nthreads = max(1, min(nthreads, B * Hq))
@@ -120,4 +139,4 @@ def attention_fwd(q, k, v, causal: bool = False, window_left: int = -1,
     else:
         with ThreadPoolExecutor(nthreads) as ex:
             list(ex.map(work, range(B * Hq)))
-    return o, lse
+    return (o, lse, mags) if tail is not None else (o, lse)

@@ -162,3 +162,20 @@ def test_oracle_is_independent_of_gpu_path():
                     src = open(os.path.join(dirpath, fn)).read()
                     assert "import oracle" not in src and "from oracle" not in src, fn
     assert oracle.attention_fwd is attention_fwd
+
+
+def test_magnitudes_bound_the_output_and_leave_it_unchanged():
+    """The optional magnitudes: P|V| dominates |O|, the tail term lies
+    between 0 and P|V| and grows with the fraction, O and lse are unchanged."""
+    q, k, v = random_inputs(850, "f32", 1, 4, 2, 90, 16, mult=2.0)
+    o, lse = attention_fwd(q, k, v, True, 30, 0.4)
+    o2, lse2, m1 = attention_fwd(q, k, v, True, 30, 0.4, tail=2 ** -10)
+    _, _, m2 = attention_fwd(q, k, v, True, 30, 0.4, tail=2 ** -4)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+    assert (np.abs(o) <= m1["pv"] * (1 + 1e-12)).all()
+    assert (m1["tail"] >= 0).all() and (m1["tail"] <= m1["pv"] * (1 + 1e-12)).all()
+    assert (m2["tail"] >= m1["tail"] - 1e-15).all() and m2["tail"].max() > m1["tail"].max()
+    # one-hot rows: nothing below the fraction, the tail is the other keys' mass
+    _, _, m0 = attention_fwd(q, k, v, True, 30, 0.4, tail=0.0)
+    np.testing.assert_array_equal(m0["tail"], 0.0)

@@ -61,3 +61,34 @@ def test_metric_flops_headline_values():
     assert W.unmasked_pairs(32768, True, 4096) == 125859840
     assert math.isclose(W.metric_flops(W.WORKLOADS["swa_32k"]), 2.0621e12, rel_tol=1e-4)
     assert W.metric_flops(W.WORKLOADS["bf16_n1k_d64"]) == 4 * 8 * 16 * 1024 ** 2 * 64
+
+
+def test_fp8_rounding_matches_torch_e4m3fn():
+    """E4M3 rounding and byte encoding agree with torch's float8_e4m3fn
+    conversion (round to nearest even) over normals, subnormals and ties."""
+    import torch
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(20000) * 40, rng.standard_normal(5000) * 0.01,
+                        np.array([0.0, -0.0, 448.0, -448.0, 2 ** -9, 2 ** -10, 3 * 2 ** -11, 2 ** -6,
+                                  1.0625, 1.1875, 17.0, 19.0, 240.0, 232.0])])
+    x = np.clip(x, -448, 448)
+    ours = W.round_to_fp8(x)
+    t = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn)
+    np.testing.assert_array_equal(ours, t.to(torch.float64).numpy())
+    np.testing.assert_array_equal(W.fp8_bits(ours), t.view(torch.uint8).numpy())
+
+
+def test_fp8_quantisation_recipe():
+    w = W.FP8_WORKLOADS["causal_8k_fp8"]
+    (qb, qs, qd), (kb, ks, kd), (vb, vs, vd) = W.make_fp8_inputs(w, B=1, Hq=1, Hkv=1, N=64)
+    for b, sc, dq in ((qb, qs, qd), (kb, ks, kd), (vb, vs, vd)):
+        assert b.dtype == np.uint8 and b.shape == (1, 1, 64, 128)
+        assert np.abs(dq).max() == pytest.approx(448 * sc, rel=1e-6)   # the largest value maps to 448
+        import torch
+        back = torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float64).numpy() * sc
+        np.testing.assert_array_equal(back, dq)
+    # quantisation is within half an E4M3 step of the float32 recipe
+    q32, _, _ = W.make_inputs(w.replace(dtype="f32"), B=1, Hq=1, Hkv=1, N=64)
+    assert np.abs(qd - q32).max() <= 2 ** -4 * np.abs(q32).max() + 1e-12
+    with pytest.raises(ValueError):
+        W.round_to_fp8(np.array([500.0]))

@@ -158,6 +158,66 @@ def bwd_metric_flops(w: Workload) -> float:
     return 2.5 * metric_flops(w)
 
 
+# ---------------------------------------------------------------------------
+# FP8 inputs (OCP E4M3: bias 7, 3 mantissa bits, no infinities, largest
+# finite 448, subnormals down to 2^-9) with one float32 scale per tensor:
+# the value a byte stands for is fp8(byte) * scale.
+
+FP8_MAX = 448.0
+
+
+def round_to_fp8(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest E4M3 value, ties to even (|x| must be <= 448)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    if (a > FP8_MAX).any():
+        raise ValueError("value beyond the E4M3 range (scale the tensor first)")
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)                 # below 2^-6: subnormal spacing 2^-9
+    ulp = np.exp2(e - 3.0)
+    r = np.round(a / ulp) * ulp            # numpy rounds half to even
+    return np.copysign(r, x)
+
+
+def fp8_bits(x: np.ndarray) -> np.ndarray:
+    """E4M3 byte of values already representable (the output of round_to_fp8)."""
+    v = np.asarray(x, dtype=np.float64)
+    a = np.abs(v)
+    sign = (np.signbit(v)).astype(np.uint8) << 7
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0))).astype(np.int64)
+    normal = a >= 2.0 ** -6
+    exp_field = np.where(normal, e + 7, 0)
+    mant = np.where(normal, (a / np.exp2(e) - 1.0) * 8.0, a / 2.0 ** -9)
+    bits = (exp_field << 3) | np.rint(mant).astype(np.int64)
+    bits = np.where(a == 0, 0, bits)
+    return (sign | bits.astype(np.uint8)).astype(np.uint8)
+
+
+def quantize_fp8(x: np.ndarray):
+    """Per-tensor quantisation: scale = max|x| / 448 (float32), bytes =
+    E4M3(x / scale).  Returns (bytes uint8, scale float, dequantised float64
+    values = fp8(bytes) * scale, which are what the method is fed)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = float(np.abs(x).max()) if x.size else 0.0
+    scale = float(np.float32(amax / FP8_MAX)) if amax > 0 else 1.0
+    q = round_to_fp8(np.clip(x.astype(np.float64) / scale, -FP8_MAX, FP8_MAX))
+    return fp8_bits(q), scale, q * scale
+
+
+FP8_WORKLOADS = {
+    # the headline shape with FP8 inputs (same seed and recipe, then quantised)
+    "causal_8k_fp8": Workload("causal_8k_fp8", "f32", 2, 16, 16, 8192, 128, True, -1, 2, value_mult=0.5),
+}
+
+
+def make_fp8_inputs(w: Workload, **over):
+    """(q, k, v) as per-tensor FP8: three (bytes, scale, dequantised) triples,
+    drawn with ``make_inputs`` of the float32 recipe, then quantised."""
+    q, k, v = make_inputs(w.replace(dtype="f32"), **over)
+    return quantize_fp8(q), quantize_fp8(k), quantize_fp8(v)
+
+
 def unmasked_pairs(N: int, causal: bool, window_left: int) -> int:
     """Number of (query i, key j) pairs that a causal and/or left-window mask
     keeps, per head: key j is kept when j <= i (if causal) and j >= i - wl
