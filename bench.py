@@ -2,7 +2,7 @@
 bf16/fp16 matrix-core peak.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload causal_8k]
-                    [--no-cpu-baseline] [--all] [--copy-calibration MiB] [--bwd]
+                    [--no-cpu-baseline] [--all] [--copy-calibration MiB] [--bwd] [--fp8]
 
 One step = one forward call (the whole path: Q/K/V tile staging, both
 contractions, online softmax, epilogue) over seeded synthetic inputs already
@@ -11,6 +11,9 @@ workload, without the CPU baseline).
 
 FLOPs credited per call: 4*d per visible (query, key) pair per head; causal
 counts N^2/2 pairs, a window counts the exact visible pairs.
+
+``--fp8`` times the FP8 forward (E4M3 inputs with per-tensor scales, bf16
+output) on the headline shape, against the dense fp8 matrix-core peak.
 
 ``--bwd`` times the backward instead (one step = one ``fa.bwd`` call: the
 row-term prep, dK/dV and dQ kernels) from the forward's o and lse, credited
@@ -28,7 +31,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense MFMA (fp32: vector/matrix)
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2, "f32": 157.3}  # dense MFMA (fp32: vector/matrix)
 KERNEL_NAME = {"bf16": "fwd_mfma_kernel", "f16": "fwd_mfma_kernel", "f32": "fwd_f32_kernel"}
 BWD_KERNELS = "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel"
 
@@ -140,6 +143,29 @@ def cpu_baseline_bwd(w, q, k, v, do, budget_s: float = 12.0):
                       f"fp64 numpy, {dt:.1f} s wall"}
 
 
+def time_steps(step, args, label, stream):
+    """W untimed calls, then K timed calls bracketed by device synchronisation.
+    Returns (wall seconds for the K calls, per-call milliseconds from HIP
+    events recorded on ``stream``, the stream the kernels are launched on)."""
+    import torch
+    print(f"[bench] {label}: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    print(f"[bench] {label}: timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
+
+
 def run_bwd(args, name, with_cpu):
     import numpy as np
     import torch
@@ -161,22 +187,7 @@ def run_bwd(args, name, with_cpu):
         fa.bwd(qd, kd, vd, o, lse, dod, causal=w.causal, window_left=w.window_left, scale=w.scale,
                dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream)
 
-    print(f"[bench] {name} bwd: warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    print(f"[bench] {name} bwd: timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_call_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
+    wall, per_call_ms = time_steps(step, args, f"{name} bwd", stream)
     avg_ms = float(np.mean(per_call_ms))
     flops = W.bwd_metric_flops(w)
     value = flops * args.steps / wall / 1e12
@@ -232,22 +243,7 @@ def run(args, name, with_cpu):
         fa.fwd(qd, kd, vd, causal=w.causal, window_left=w.window_left, scale=w.scale,
                out=o, lse=lse, stream=stream)
 
-    print(f"[bench] {name}: warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    print(f"[bench] {name}: timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    wall, per_launch_ms = time_steps(step, args, name, stream)
     avg_ms = float(np.mean(per_launch_ms))
     flops = W.metric_flops(w)
     value = flops * args.steps / wall / 1e12
@@ -286,6 +282,63 @@ def run(args, name, with_cpu):
     return rec
 
 
+def run_fp8(args, name, with_cpu):
+    """The FP8 forward on its workload: E4M3 inputs with per-tensor scales
+    (the float32 recipe quantised on the host), bf16 output, lse."""
+    import numpy as np
+    import torch
+
+    import exact_tiled_attention_04_amd as fa
+    import workloads as W
+
+    w = W.FP8_WORKLOADS[name]
+    (qb, qs, qf), (kb, ks, kf), (vb, vs, vf) = W.make_fp8_inputs(w)
+    qd, kd, vd = (torch.from_numpy(x).cuda() for x in (qb, kb, vb))
+    o = torch.empty(qd.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fa.fwd_fp8(qd, kd, vd, qs, ks, vs, causal=w.causal, window_left=w.window_left, scale=w.scale,
+                   out=o, lse=lse, stream=stream)
+
+    wall, per_launch_ms = time_steps(step, args, name, stream)
+    avg_ms = float(np.mean(per_launch_ms))
+    flops = W.metric_flops(w)
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["fp8"]
+    rec = {
+        "metric": "attention fwd TFLOP/s + % of MI355X fp8 MFMA peak (FP8 E4M3 inputs, d=128, causal, N=8k)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "window_left": w.window_left, "scale": w.scale, "seed": w.seed,
+                   "scales": [qs, ks, vs], "output": "bf16", "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": "fwd_fp8_kernel",
+                     "avg_launch_us": round(avg_ms * 1e3, 2),
+                     "min_launch_us": round(float(np.min(per_launch_ms)) * 1e3, 2)},
+    }
+    copy_note = calibration_copy(args.copy_calibration)
+    if copy_note:
+        rec["calibration"] = copy_note
+    if with_cpu:
+        print(f"[bench] {name}: cpu baseline (oracle on the dequantised inputs)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, qf, kf, vf)
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,6 +354,7 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="also run a device copy of this size (counter calibration)")
     ap.add_argument("--bwd", action="store_true", help="time the backward pass instead of the forward")
+    ap.add_argument("--fp8", action="store_true", help="time the FP8 forward (workload causal_8k_fp8)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the forward kernel runs on a single device "
@@ -312,6 +366,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     import workloads as W
+    if args.fp8:
+        name = args.workload if args.workload in W.FP8_WORKLOADS else "causal_8k_fp8"
+        print(json.dumps(run_fp8(args, name, not args.no_cpu_baseline)), flush=True)
+        return
     if args.bwd:
         names = [n for n in W.ORDER if W.WORKLOADS[n].dtype != "f32"] if args.all else [args.workload]
         for name in names:

@@ -5,7 +5,8 @@ The computation lives in ``libfa.so`` (HIP kernels for gfx950 behind the C ABI
 of ``include/fa.h``).  This package is a thin binding:
 
     _lib        the C entry points under their C names (raw addresses, sizes)
-    attention   ``fwd(q, k, v, causal, window_left, scale)`` and
+    attention   ``fwd(q, k, v, causal, window_left, scale)``,
+                ``fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, ...)`` and
                 ``bwd(q, k, v, o, lse, dout, ...)`` on torch tensors
     build       compiles libfa.so in-tree with hipcc
 """
@@ -17,9 +18,14 @@ def fwd(*args, **kwargs):
     return _fwd(*args, **kwargs)
 
 
+def fwd_fp8(*args, **kwargs):
+    from .attention import fwd_fp8 as _fwd_fp8
+    return _fwd_fp8(*args, **kwargs)
+
+
 def bwd(*args, **kwargs):
     from .attention import bwd as _bwd
     return _bwd(*args, **kwargs)
 
 
-__all__ = ["fwd", "bwd", "FaError", "LIB_PATH", "load"]
+__all__ = ["fwd", "fwd_fp8", "bwd", "FaError", "LIB_PATH", "load"]

@@ -22,7 +22,7 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_MISALIGNED = -3
 FA_ERR_HIP = -4
 
-EXPORTED = ["fa_fwd", "fa_fwd_bf16", "fa_fwd_f16", "fa_fwd_f32", "fa_bwd", "fa_bwd_bf16", "fa_bwd_f16",
+EXPORTED = ["fa_fwd", "fa_fwd_bf16", "fa_fwd_f16", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_bwd_bf16", "fa_bwd_f16",
             "fa_bwd_workspace_size", "fa_status_string", "fa_last_error", "fa_version"]
 
 _lock = threading.Lock()
@@ -55,6 +55,8 @@ def load() -> ctypes.CDLL:
             fn.restype = I
         lib.fa_fwd.argtypes = fwd_args + [I]
         lib.fa_fwd.restype = I
+        lib.fa_fwd_fp8.argtypes = [P, P, P, F, F, F, P, P, I, I, I, I, I, I, I, F, P]
+        lib.fa_fwd_fp8.restype = I
         bwd_args = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
         for name in ("fa_bwd_bf16", "fa_bwd_f16"):
             fn = getattr(lib, name)
@@ -96,6 +98,12 @@ def fa_fwd_f16(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window_left, scale, st
 def fa_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window_left, scale, stream) -> int:
     return load().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
                              int(bool(causal)), window_left, scale, _ptr(stream))
+
+
+def fa_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, d, causal, window_left, scale,
+               stream) -> int:
+    return load().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), q_scale, k_scale, v_scale, _ptr(o), _ptr(lse), B, Hq, Hkv,
+                             N, d, int(bool(causal)), window_left, scale, _ptr(stream))
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, causal, window_left, scale, stream,

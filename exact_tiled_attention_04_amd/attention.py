@@ -58,6 +58,54 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     return o, lse
 
 
+_BYTE_TYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_scale: float, k_scale: float, v_scale: float,
+            causal: bool = False, window_left: int = -1, scale: Optional[float] = None,
+            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+            stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Exact attention forward on FP8 (E4M3) inputs with per-tensor scales.
+
+    q: [B, Hq, N, d]; k, v: [B, Hkv, N, d]; contiguous torch.float8_e4m3fn
+    (or uint8 holding the same bytes) on one GPU; element x stands for
+    e4m3(x) * x_scale.  Returns (o, lse): o bfloat16 shaped like q, lse
+    float32 [B, Hq, N] (None when want_lse is False and no lse is given).
+    Asynchronous on ``stream`` (default: the current stream).  Raises
+    _lib.FaError when the library rejects the arguments.
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    if any(t.dtype not in _BYTE_TYPES for t in (q, k, v)):
+        raise ValueError("q, k, v must be float8_e4m3fn (or uint8 bytes)")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on one GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, Hq, N, d = q.shape
+    if tuple(k.shape) != (B, k.shape[1], N, d) or k.shape != v.shape:
+        raise ValueError("k and v must be [B, Hkv, N, d] with q's B, N, d")
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = out if out is not None else torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, Hq, N) or lse.dtype != torch.float32
+                            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, N] tensor")
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        status = _lib.fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), float(q_scale), float(k_scale),
+                                 float(v_scale), o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                 B, Hq, Hkv, N, d, causal, window_left, float(scale), s.cuda_stream)
+    if status != _lib.FA_OK:
+        raise _lib.FaError(status, _lib.fa_last_error())
+    return o, lse
+
+
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
         dout: torch.Tensor, causal: bool = False, window_left: int = -1, scale: Optional[float] = None,
         dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,

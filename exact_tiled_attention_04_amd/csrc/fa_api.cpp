@@ -118,6 +118,62 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   return FA_OK;
 }
 
+int run_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale, float v_scale, void* o,
+            float* lse, int B, int Hq, int Hkv, int N, int d, int causal, int window_left, float scale,
+            void* stream) {
+  g_last_error[0] = '\0';
+  bool empty;
+  if (int st = check_sizes(B, Hq, Hkv, N, d, window_left, scale, FA_DTYPE_BF16, &empty)) return st;
+  if (empty) return FA_OK;
+  if (!std::isfinite(q_scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale) || !(q_scale > 0.f) ||
+      !(k_scale > 0.f) || !(v_scale > 0.f))
+    return fail(FA_ERR_INVALID_ARG, "the FP8 scales must be finite and > 0 (q %g, k %g, v %g)", (double)q_scale,
+                (double)k_scale, (double)v_scale);
+  const double c = (double)scale * q_scale * k_scale;
+  if (!(c < 1e30))
+    return fail(FA_ERR_INVALID_ARG, "scale * q_scale * k_scale = %g is out of range", c);
+  if (!q || !k || !v || !o)
+    return fail(FA_ERR_INVALID_ARG, "null q/k/v/o pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(FA_ERR_MISALIGNED, "q, k, v and o must be 16-byte aligned");
+  if (lse && !aligned(lse, 4))
+    return fail(FA_ERR_MISALIGNED, "lse must be 4-byte aligned");
+  const uint64_t n_q = (uint64_t)B * Hq * N * d;
+  const uint64_t n_kv = (uint64_t)B * Hkv * N * d;
+  const uint64_t n_o = 2 * n_q;
+  if (overlap(o, n_o, q, n_q) || overlap(o, n_o, k, n_kv) || overlap(o, n_o, v, n_kv))
+    return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
+  if (lse) {
+    const uint64_t n_l = (uint64_t)B * Hq * N * sizeof(float);
+    if (overlap(lse, n_l, o, n_o) || overlap(lse, n_l, q, n_q) || overlap(lse, n_l, k, n_kv) ||
+        overlap(lse, n_l, v, n_kv))
+      return fail(FA_ERR_INVALID_ARG, "lse overlaps o or an input");
+  }
+  if ((uint64_t)N * d + (1u << 20) > (uint64_t)INT32_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "N=%d too long for d=%d (one head must stay below 2 GiB)", N, d);
+  const long long rows = fa::fp8_rows_per_workgroup();
+  const long long items = (long long)B * Hq * ((N + rows - 1) / rows);
+  if (items > fa::kMaxGridItems)
+    return fail(FA_ERR_UNSUPPORTED, "B*Hq*ceil(N/%lld)=%lld exceeds one launch", rows, items);
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.N = N;
+  a.d = d;
+  a.causal = causal;
+  a.window_left = window_left;
+  a.scale = scale;
+  const hipError_t e = fa::launch_fwd_fp8(a, q_scale, k_scale, v_scale, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
 uint64_t bwd_workspace_bytes(int B, int Hq, int N) {
   return B <= 0 || Hq <= 0 || N <= 0 ? 0 : 2ull * (uint64_t)B * Hq * N * sizeof(float);
 }
@@ -209,6 +265,12 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
   return run(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window_left, scale, stream, FA_DTYPE_F32);
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale, float v_scale, void* o,
+               float* lse, int B, int Hq, int Hkv, int N, int d, int causal, int window_left, float scale,
+               void* stream) {
+  return run_fp8(q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, d, causal, window_left, scale, stream);
+}
+
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
            void* dq, void* dk, void* dv, float* workspace, int B, int Hq, int Hkv, int N, int d, int causal,
            int window_left, float scale, void* stream, fa_dtype_t dtype) {
@@ -245,6 +307,6 @@ const char* fa_status_string(int status) {
 
 const char* fa_last_error(void) { return g_last_error; }
 
-int fa_version(void) { return 200; }  // 0.2.0
+int fa_version(void) { return 300; }  // 0.3.0
 
 }  // extern "C"

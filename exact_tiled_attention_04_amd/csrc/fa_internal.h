@@ -33,6 +33,8 @@ struct FwdParams {
   int n_qblocks;     // ceil(N / rows per workgroup)
   int total_items;   // B * Hq * n_qblocks
   float scale_log2;  // scale * log2(e): scores go straight into exp2
+                     // (FP8: times the Q and K scales)
+  float o_mult;      // multiplier on the output: the V scale of FP8 inputs, else 1
 };
 
 // Workgroup -> (batch*head, query block) mapping.
@@ -93,6 +95,7 @@ inline FwdParams make_params(const FwdArgs& a, int rows_per_wg) {
   p.n_qblocks = (a.N + rows_per_wg - 1) / rows_per_wg;
   p.total_items = a.B * a.Hq * p.n_qblocks;
   p.scale_log2 = a.scale * 1.4426950408889634f;
+  p.o_mult = 1.f;
   return p;
 }
 
@@ -174,10 +177,13 @@ long long bwd_rows_per_workgroup();
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+// q, k, v hold E4M3 bytes standing for byte * scale; o is bfloat16.
+hipError_t launch_fwd_fp8(const FwdArgs& a, float q_scale, float k_scale, float v_scale, hipStream_t stream);
 
 // Query rows handled by one workgroup of each kernel.
 long long mfma_rows_per_workgroup();
 long long f32_rows_per_workgroup();
+long long fp8_rows_per_workgroup();
 
 // Largest B*Hq*n_qblocks a single launch accepts (grid.x limit).
 constexpr long long kMaxGridItems = 2147483647LL;

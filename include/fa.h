@@ -107,6 +107,43 @@ int fa_fwd_f32(const void *q, const void *k, const void *v, void *o, float *lse,
                float scale, void *stream);
 
 /*
+ * Attention forward on FP8 inputs with per-tensor scales.
+ *
+ * The FlashAttention quiz (question 6) and the FlashAttention-2 (PL) article
+ * (section "FlashAttention-3") name 8-bit floating point, with its rounding
+ * error kept in check, as a further speed-up.  Here q, k and v hold OCP E4M3
+ * bytes (bias 7, 3 mantissa bits, largest finite 448, no infinities; the
+ * torch.float8_e4m3fn encoding) and each tensor has one float32 scale: an
+ * element stands for e4m3(byte) * x_scale.  The operation is fa_fwd's on those
+ * values, with
+ *
+ *     s_ij = scale * q_scale * k_scale * sum_c e4m3(q_ic) * e4m3(k_jc)
+ *     o    = v_scale * sum_j softmax_j(s_i.) * e4m3(v_j)
+ *
+ * Both products run on the FP8 matrix cores and accumulate in fp32; the
+ * probabilities are rounded to E4M3 for the second product (the row sum is
+ * taken before that rounding), so o carries an error of at most about 2^-4
+ * of sum_j p_ij |v_j|, plus the rounding of o to bfloat16.
+ *
+ *   q, k, v      E4M3 bytes (device), layouts above with 1-byte elements.
+ *                The NaN bytes 0x7f and 0xff are not valid inputs: rows whose
+ *                key tiles hold one may come out NaN.
+ *   q_scale, k_scale, v_scale
+ *                per-tensor dequantisation scales, finite and > 0.
+ *   o            output (device), bfloat16, layout of q.
+ *   lse          output (device) float32 [B][Hq][N] (natural log of the sum
+ *                of exp(s_ij) over visible keys), or NULL to skip it.
+ *   B ... stream as for fa_fwd.
+ *
+ * Errors and ownership as for fa_fwd; in addition a scale that is not finite
+ * and positive, or whose product with scale overflows, is FA_ERR_INVALID_ARG.
+ */
+int fa_fwd_fp8(const void *q, const void *k, const void *v,
+               float q_scale, float k_scale, float v_scale, void *o, float *lse,
+               int B, int Hq, int Hkv, int N, int d, int causal, int window_left,
+               float scale, void *stream);
+
+/*
  * Gradients of fa_fwd's output with respect to q, k and v.
  *
  * For an upstream gradient dout = dL/do (the logsumexp output is taken to

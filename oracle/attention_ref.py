@@ -54,6 +54,7 @@ def _one_head(qh, kh, vh, rows, causal, window_left, scale, tail=None):
     out_l = np.empty(len(rows), dtype=np.float64)
     mag_pv = np.empty((len(rows), d), dtype=np.float64) if tail is not None else None
     mag_tail = np.empty((len(rows), d), dtype=np.float64) if tail is not None else None
+    mag_s = np.empty(len(rows), dtype=np.float64) if tail is not None else None
     keys = np.arange(N)
     for s0 in range(0, len(rows), ROW_BLOCK):
         r = rows[s0:s0 + ROW_BLOCK]
@@ -72,8 +73,11 @@ def _one_head(qh, kh, vh, rows, causal, window_left, scale, tail=None):
             mag_pv[s0:s0 + len(r)] = P @ np.abs(vh)
             small = np.minimum(P, tail * P.max(axis=1, keepdims=True))
             mag_tail[s0:s0 + len(r)] = small @ np.abs(vh)
+            A = scale * (np.abs(qh[r]) @ np.abs(kh).T)
+            A[masked(r[:, None], keys[None, :], causal, window_left)] = 0.0
+            mag_s[s0:s0 + len(r)] = A.max(axis=1)
     if tail is not None:
-        return out_o, out_l, mag_pv, mag_tail
+        return out_o, out_l, mag_pv, mag_tail, mag_s
     return out_o, out_l
 
 
@@ -90,7 +94,9 @@ def attention_fwd(q, k, v, causal: bool = False, window_left: int = -1,
     With ``tail`` (a fraction), also returns a dict of magnitudes for error
     bounds, shaped like o: 'pv' = P|V| and 'tail' = sum_j min(p_ij, tail *
     max_j p_ij) |v_j| (the mass of probabilities below that fraction of their
-    row's largest, as if dropped, bounded by it).
+    row's largest, as if dropped, bounded by it), shaped like o, and 'sabs' =
+    max over visible j of scale * sum_c |q_ic| |k_jc|, shaped like lse (a
+    bound on every visible score's size and on what its sum accumulates).
 
     Raises ValueError on inconsistent shapes, Hq not a multiple of Hkv, or
     window_left < -1.  Every row has at least one visible key (key j = i is
@@ -116,7 +122,7 @@ def attention_fwd(q, k, v, causal: bool = False, window_left: int = -1,
     R = len(rows)
     o = np.empty((B, Hq, R, d), dtype=np.float64)
     lse = np.empty((B, Hq, R), dtype=np.float64)
-    mags = {"pv": np.empty_like(o), "tail": np.empty_like(o)} if tail is not None else None
+    mags = {"pv": np.empty_like(o), "tail": np.empty_like(o), "sabs": np.empty_like(lse)} if tail is not None else None
     if B * Hq * R == 0:
         return (o, lse, mags) if tail is not None else (o, lse)
 
@@ -129,7 +135,7 @@ def attention_fwd(q, k, v, causal: bool = False, window_left: int = -1,
         res = _one_head(qh, kh, vh, rows, causal, window_left, scale, tail)
         o[b, h], lse[b, h] = res[0], res[1]
         if tail is not None:
-            mags["pv"][b, h], mags["tail"][b, h] = res[2], res[3]
+            mags["pv"][b, h], mags["tail"][b, h], mags["sabs"][b, h] = res[2], res[3], res[4]
 
     nthreads = threads or len(os.sched_getaffinity(0))
     nthreads = max(1, min(nthreads, B * Hq))

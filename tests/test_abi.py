@@ -162,3 +162,42 @@ def test_bwd_typed_entry_points_and_workspace_size():
     assert _lib.fa_bwd_workspace_size(2, 16, 8192) == 2 * 2 * 16 * 8192 * 4
     assert _lib.fa_bwd_workspace_size(0, 16, 8192) == 0
     assert _lib.fa_bwd_workspace_size(1, -1, 10) == 0
+
+
+# FP8 forward: fake addresses; every case fails (or no-ops) before a launch
+GOOD_FP8 = dict(q=Q, k=K, v=V, qs=0.01, ks=0.02, vs=0.03, o=O, lse=L, B=1, Hq=4, Hkv=2, N=16, d=64, causal=0,
+                window_left=-1, scale=0.125, stream=None)
+
+
+def call_fp8(**over):
+    a = dict(GOOD_FP8, **over)
+    return _lib.fa_fwd_fp8(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["o"], a["lse"], a["B"], a["Hq"],
+                           a["Hkv"], a["N"], a["d"], a["causal"], a["window_left"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(B=-1), _lib.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), _lib.FA_ERR_INVALID_ARG),
+    (dict(window_left=-2), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), _lib.FA_ERR_UNSUPPORTED),
+    (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
+    (dict(qs=0.0), _lib.FA_ERR_INVALID_ARG),
+    (dict(ks=-1.0), _lib.FA_ERR_INVALID_ARG),
+    (dict(vs=float("inf")), _lib.FA_ERR_INVALID_ARG),
+    (dict(vs=float("nan")), _lib.FA_ERR_INVALID_ARG),
+    (dict(qs=1e20, ks=1e20), _lib.FA_ERR_INVALID_ARG),   # scale * q_scale * k_scale overflows
+    (dict(v=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(k=K + 8), _lib.FA_ERR_MISALIGNED),
+    (dict(lse=L + 1), _lib.FA_ERR_MISALIGNED),
+    (dict(o=K - 1024), _lib.FA_ERR_INVALID_ARG),   # o (2 bytes per element) runs into k
+    (dict(lse=O + 2048 - 4), _lib.FA_ERR_INVALID_ARG),   # lse inside o's 2-byte span
+])
+def test_fp8_validation_rejects(over, status):
+    assert call_fp8(**over) == status
+    assert _lib.fa_last_error() != ""
+
+
+def test_fp8_empty_problem_is_a_noop():
+    assert call_fp8(B=0, q=0, k=0, v=0, o=0, lse=0) == _lib.FA_OK
+    assert call_fp8(N=0) == _lib.FA_OK

@@ -176,6 +176,17 @@ def test_magnitudes_bound_the_output_and_leave_it_unchanged():
     assert (np.abs(o) <= m1["pv"] * (1 + 1e-12)).all()
     assert (m1["tail"] >= 0).all() and (m1["tail"] <= m1["pv"] * (1 + 1e-12)).all()
     assert (m2["tail"] >= m1["tail"] - 1e-15).all() and m2["tail"].max() > m1["tail"].max()
-    # one-hot rows: nothing below the fraction, the tail is the other keys' mass
+    # a zero fraction leaves no tail
     _, _, m0 = attention_fwd(q, k, v, True, 30, 0.4, tail=0.0)
     np.testing.assert_array_equal(m0["tail"], 0.0)
+    # sabs bounds every visible score, and is the largest one for
+    # nonnegative inputs (brute force over the visible keys)
+    qa, ka, va = np.abs(q).astype(np.float64), np.abs(k).astype(np.float64), v
+    _, _, ma = attention_fwd(qa, ka, va, True, 30, 0.4, tail=0.0)
+    for b, h, i in [(0, 0, 0), (0, 1, 45), (0, 3, 89), (0, 2, 31)]:
+        hk = h // 2
+        js = [j for j in range(90) if j <= i and j >= i - 30]
+        s_pos = max(0.4 * float(qa[b, h, i] @ ka[b, hk, j]) for j in js)
+        assert abs(ma["sabs"][b, h, i] - s_pos) <= 1e-12 * s_pos
+        s_abs = max(abs(0.4 * float(q[b, h, i].astype(np.float64) @ k[b, hk, j])) for j in js)
+        assert m1["sabs"][b, h, i] >= s_abs
