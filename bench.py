@@ -36,29 +36,30 @@ KERNEL_NAME = {"bf16": "fwd_mfma_kernel", "f16": "fwd_mfma_kernel", "f32": "fwd_
 BWD_KERNELS = "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel"
 
 
-# sources the forward kernel is compiled from (its launch, host code aside)
+# sources each forward kernel is compiled from (its launch, host code aside)
 FWD_SOURCES = ("fa_fwd_mfma.hip", "fa_mfma_common.h", "fa_internal.h")
+FP8_SOURCES = ("fa_fwd_fp8.hip", "fa_mfma_common.h", "fa_internal.h")
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the forward kernel's sources (sorted by name): a stored
-    traffic measurement stays valid while these are unchanged."""
+def kernel_source_hash(sources=FWD_SOURCES) -> str:
+    """sha256 over a kernel's sources (sorted by name): a stored traffic
+    measurement stays valid while these are unchanged."""
     csrc = os.path.join(ROOT, "exact_tiled_attention_04_amd", "csrc")
     h = hashlib.sha256()
-    for fn in sorted(FWD_SOURCES):
+    for fn in sorted(sources):
         h.update(fn.encode())
         h.update(open(os.path.join(csrc, fn), "rb").read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, sources=FWD_SOURCES):
     """HBM bytes per launch from the committed counter summary, or None when
     absent or taken on different kernel sources."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    if rec.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -326,7 +327,8 @@ def run_fp8(args, name, with_cpu):
                    "causal": w.causal, "window_left": w.window_left, "scale": w.scale, "seed": w.seed,
                    "scales": [qs, ks, vs], "output": "bf16", "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": "fwd_fp8_kernel",
+                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(name, FP8_SOURCES),
+                     "kernel": "fwd_fp8_kernel",
                      "avg_launch_us": round(avg_ms * 1e3, 2),
                      "min_launch_us": round(float(np.min(per_launch_ms)) * 1e3, 2)},
     }

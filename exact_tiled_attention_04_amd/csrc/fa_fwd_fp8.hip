@@ -58,6 +58,12 @@ constexpr int kBR = kWaves * kRowsPerWave;  // query rows per workgroup
 #ifndef FA8_KEYS_PER_TILE
 #define FA8_KEYS_PER_TILE 64
 #endif
+// Three waves per SIMD at d = 128 (the register budget of 168 costs a few
+// spilled registers and still wins over two waves); d = 64 needs fewer
+// registers and reaches four either way.
+#ifndef FA8_WAVES_PER_SIMD
+#define FA8_WAVES_PER_SIMD 3
+#endif
 constexpr int kBC = FA8_KEYS_PER_TILE;  // keys per K/V tile
 constexpr int kHalves = kBC / 32;       // 32-key score blocks per tile
 constexpr int kBlocks64 = kBC / 64;     // 64-key probability blocks per tile
@@ -232,6 +238,17 @@ __device__ __forceinline__ float max_tree(const float (&a)[N]) {
   }
 }
 
+// Sum of N values as a balanced tree of two-input adds (depth log2 N
+// instead of a serial chain of N - 1 dependent adds).
+template <int N>
+__device__ __forceinline__ float sum_tree(const float* a) {
+  if constexpr (N == 1) {
+    return a[0];
+  } else {
+    return sum_tree<N / 2>(a) + sum_tree<N - N / 2>(a + N / 2);
+  }
+}
+
 // Online softmax of one score tile: turns s into the E4M3 probability
 // operands pf (8 dwords per 64-key block), updates the row's reference max
 // and sum, and returns the factor the partial output must be multiplied by.
@@ -254,15 +271,15 @@ __device__ __forceinline__ float tile_softmax(const LoopCtx<D>& x, RowState<D>& 
   const float alpha = bump ? __builtin_amdgcn_exp2f(st.m_use - mx) : 1.f;
   st.m_use = bump ? mx : st.m_use;
   const float m_exp = (st.m_use == -INFINITY) ? 0.f : st.m_use - kPOffset;
-  float rs = 0.f;
 #pragma unroll
   for (int h = 0; h < kHalves; ++h) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       s[h][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][i], x.c, -m_exp));
-      rs += s[h][i];
+      sv[16 * h + i] = s[h][i];
     }
   }
+  const float rs = sum_tree<16 * kHalves>(sv);
   st.l_run = __builtin_fmaf(st.l_run, alpha, rs);
   // dword w of block b packs keys of s[2b + w/4], elements 4(w%4) .. +3
 #pragma unroll
@@ -351,7 +368,7 @@ __device__ __forceinline__ void tile_barrier() {
 }
 
 template <int D>
-__global__ void __launch_bounds__(kThreads, 2) fwd_fp8_kernel(FwdParams p) {
+__global__ void __launch_bounds__(kThreads, FA8_WAVES_PER_SIMD) fwd_fp8_kernel(FwdParams p) {
   using S = Shape<D>;
   __shared__ __attribute__((aligned(16))) unsigned char sK0[kBC * D];
   __shared__ __attribute__((aligned(16))) unsigned char sK1[kBC * D];
@@ -450,7 +467,9 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_fp8_kernel(FwdParams p) {
     if (t + 4 < x.t_end) step(std::integral_constant<int, 5>{}, t + 4);
     if (t + 5 < x.t_end) step(std::integral_constant<int, 0>{}, t + 5);
   }
-  tile_barrier<kInFlight>();
+  // drain: P(t_end-1) V(t_end-1); wait for every copy, so that none is still
+  // in flight into LDS when the workgroup ends
+  tile_barrier<0>();
   rescale_if_needed(alpha_prev, st.oacc, S::kOutTiles);
   if ((x.t_end - 1 - t0) % 2 == 0)
     tile_pv<D>(sV0, x, st, pf_prev);

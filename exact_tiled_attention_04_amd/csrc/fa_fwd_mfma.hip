@@ -491,8 +491,9 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) fwd_mfma_kernel(FwdPa
     if (t + 4 < x.t_end) step(std::integral_constant<int, 5>{}, t + 4);
     if (t + 5 < x.t_end) step(std::integral_constant<int, 0>{}, t + 5);
   }
-  // drain: P(t_end-1) V(t_end-1)
-  tile_barrier<kInFlight>();
+  // drain: P(t_end-1) V(t_end-1); wait for every copy, so that none is still
+  // in flight into LDS when the workgroup ends
+  tile_barrier<0>();
   rescale_if_needed(alpha_prev, st.oacc, S::kOutTiles);
   const int rl = (x.t_end - 1 - t0) % kVBufs;
   if (rl == 0)

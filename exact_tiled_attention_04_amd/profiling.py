@@ -14,7 +14,9 @@ files under ``profiles/``.
 --pmc     further counter-collection directories (SQ_*/GRBM_* counters), summed
           per dispatch of the attention kernel
 --last    use only the last N dispatches of the kernel (the timed steps)
---kernel  substring selecting the kernel (default: the forward, "fwd_")
+--kernel  substring selecting the kernel (default: the forward, "fwd_";
+          "fwd_fp8" with --fp8 for the FP8 forward)
+--peak    TFLOP/s the algorithmic FLOPs are priced against (default 2516.6)
 --name    output base name (default: fwd_<workload>; the traffic JSON that
           bench.py reads is written only for the forward)
 """
@@ -32,16 +34,17 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_KEY = "fwd_"
 
 
-# sources the forward kernel is compiled from (its launch, host code aside)
+# sources each forward kernel is compiled from (its launch, host code aside)
 FWD_SOURCES = ("fa_fwd_mfma.hip", "fa_mfma_common.h", "fa_internal.h")
+FP8_SOURCES = ("fa_fwd_fp8.hip", "fa_mfma_common.h", "fa_internal.h")
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the forward kernel's sources (sorted by name): a stored
-    traffic measurement stays valid while these are unchanged."""
+def kernel_source_hash(sources=FWD_SOURCES) -> str:
+    """sha256 over a kernel's sources (sorted by name): a stored traffic
+    measurement stays valid while these are unchanged."""
     csrc = os.path.join(ROOT, "exact_tiled_attention_04_amd", "csrc")
     h = hashlib.sha256()
-    for fn in sorted(FWD_SOURCES):
+    for fn in sorted(sources):
         h.update(fn.encode())
         h.update(open(os.path.join(csrc, fn), "rb").read())
     return h.hexdigest()
@@ -109,11 +112,14 @@ def main():
     ap.add_argument("--kernel", default="fwd_")
     ap.add_argument("--name", default=None)
     ap.add_argument("--flops", type=float, default=None, help="algorithmic FLOPs per launch")
+    ap.add_argument("--peak", type=float, default=2516.6, help="peak TFLOP/s the FLOPs are priced against")
+    ap.add_argument("--fp8", action="store_true", help="the FP8 forward kernel (its sources for the hash)")
     ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     args = ap.parse_args()
     global KERNEL_KEY
     KERNEL_KEY = args.kernel
-    forward = args.kernel == "fwd_"
+    forward = args.kernel in ("fwd_", "fwd_fp8")
+    sources = FP8_SOURCES if args.fp8 else FWD_SOURCES
     name = args.name or f"fwd_{args.workload}"
 
     tr = trace_summary(args.trace, args.last)
@@ -128,8 +134,8 @@ def main():
               f"min {tr['min_us']:.1f} us, max {tr['max_us']:.1f} us"]
     if args.flops:
         lines.append(f"algorithmic FLOPs per launch {args.flops:.4e} -> {args.flops / (tr['avg_us'] * 1e-6) / 1e12:.1f} "
-                     f"TFLOP/s at the average duration ({100 * args.flops / (tr['avg_us'] * 1e-6) / 2516.6e12:.1f}% "
-                     f"of 2516.6 TFLOP/s)")
+                     f"TFLOP/s at the average duration ({100 * args.flops / (tr['avg_us'] * 1e-6) / (args.peak * 1e12):.1f}% "
+                     f"of {args.peak} TFLOP/s)")
     traffic = None
     if args.fetch and args.write and args.copy_mib:
         copy_bytes = args.copy_mib * 2 ** 20
@@ -150,7 +156,7 @@ def main():
                   f"-> {write_b / 2**20:.1f} MiB written",
                   f"  total {traffic / 2**20:.1f} MiB per launch"]
         if forward:
-            json.dump({"workload": args.workload, "kernel_source_sha256": kernel_source_hash(),
+            json.dump({"workload": args.workload, "kernel_source_sha256": kernel_source_hash(sources),
                        "hbm_bytes_per_launch": round(traffic), "fetch_bytes": round(fetch_b),
                        "write_bytes": round(write_b), "fetch_scale": f_scale, "write_scale": w_scale,
                        "commands": args.command},
@@ -170,7 +176,7 @@ def main():
         if "SQ_LDS_BANK_CONFLICT" in a and "SQ_LDS_IDX_ACTIVE" in a:
             bc = statistics.mean(a["SQ_LDS_BANK_CONFLICT"]) / max(1.0, statistics.mean(a["SQ_LDS_IDX_ACTIVE"]))
             lines.append(f"  LDS bank-conflict cycles / LDS active cycles = {100 * bc:.2f}%")
-    lines.append(f"\nkernel sources sha256 {kernel_source_hash()}")
+    lines.append(f"\nkernel sources sha256 {kernel_source_hash(sources)}")
     out = os.path.join(args.out_dir, f"{name}.md")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
