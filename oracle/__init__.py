@@ -14,6 +14,9 @@ Contents
 ``online_emul``    the tiled method itself in fp64: query and key/value blocks,
                    a running max and running sum per row, rescaling of the
                    partial output, one division at the end.
+``attention_kvcache_ref``  the same attention for a few query rows against a
+                   key/value cache of per-batch length (rows aligned to the
+                   end of the cache), as in decoding.
 ``attention_bwd_ref``  fp64 gradients dQ, dK, dV of the forward above for an
                    upstream gradient dO (chain rule through O = P V and the
                    row softmax; P rebuilt per block of rows), with optional
@@ -42,9 +45,12 @@ Every function here is pinned by tests in ``tests/test_oracle.py`` against
 closed forms, invariants, hand-worked fixtures and an independent library
 routine (torch's CPU scaled-dot-product attention in float64); the gradients
 are pinned in ``tests/test_oracle_bwd.py`` against central finite differences
-of the forward oracle, torch's float64 autograd, and closed forms.
+of the forward oracle, torch's float64 autograd, and closed forms; the cache
+form in ``tests/test_oracle_kvcache.py`` against the last rows of the full
+forward oracle, a loop-by-loop brute force, and closed forms.
 """
 from .attention_ref import attention_fwd, masked, kv_head_of  # noqa: F401
 from .twopass_ref import attention_twopass  # noqa: F401
 from .online_emul import attention_online  # noqa: F401
 from .attention_bwd_ref import attention_bwd  # noqa: F401
+from .attention_kvcache_ref import attention_fwd_kvcache  # noqa: F401
