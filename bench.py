@@ -2,7 +2,7 @@
 bf16/fp16 matrix-core peak.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload causal_8k]
-                    [--no-cpu-baseline] [--all] [--copy-calibration MiB] [--bwd] [--fp8]
+                    [--no-cpu-baseline] [--all] [--copy-calibration MiB] [--bwd] [--fp8] [--decode [--splits S]]
 
 One step = one forward call (the whole path: Q/K/V tile staging, both
 contractions, online softmax, epilogue) over seeded synthetic inputs already
@@ -14,6 +14,10 @@ counts N^2/2 pairs, a window counts the exact visible pairs.
 
 ``--fp8`` times the FP8 forward (E4M3 inputs with per-tensor scales, bf16
 output) on the headline shape, against the dense fp8 matrix-core peak.
+
+``--decode`` times attention against a key/value cache (few query rows per
+sequence, split-KV plus merge) on ``decode_gqa_32k`` (``--all``: every
+decoding workload), as algorithmic bytes per second against HBM bandwidth.
 
 ``--bwd`` times the backward instead (one step = one ``fa.bwd`` call: the
 row-term prep, dK/dV and dQ kernels) from the forward's o and lse, credited
@@ -341,6 +345,110 @@ def run_fp8(args, name, with_cpu):
     return rec
 
 
+def cpu_baseline_decode(w, q, k, v, lens, budget_s: float = 12.0):
+    """The fp64 cache oracle, as it stands, on a bounded sample: whole
+    batches (every head, every row), one worker thread per host core, until
+    ``budget_s`` of wall time has passed; reported as GB/s of the same
+    algorithmic bytes the GPU line counts."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import workloads as W
+    from oracle import attention_fwd_kvcache
+
+    cores = len(os.sched_getaffinity(0))
+    done, nbytes = 0, 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while done < w.B and time.perf_counter() - t0 < budget_s:
+            b = done
+            attention_fwd_kvcache(q[b:b + 1], k[b:b + 1], v[b:b + 1], lens[b:b + 1], w.causal, w.window_left,
+                                  w.scale, threads=cores)
+            nbytes += W.decode_bytes(w.replace(B=1), lens[b:b + 1])
+            done += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": min(cores, w.Hq), "kind": "oracle",
+            "sample": f"{done} of {w.B} sequences (every head and row), fp64 numpy, {dt:.1f} s wall"}
+
+
+def run_decode(args, name, with_cpu):
+    """Attention against a key/value cache: one step = one fa.fwd_kvcache(_paged)
+    call (the split kernel and, with more than one split, the merge), cache
+    resident in device memory.  Metric: algorithmic bytes per second."""
+    import numpy as np
+    import torch
+
+    import exact_tiled_attention_04_amd as fa
+    import workloads as W
+
+    w = W.DECODE_WORKLOADS[name]
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    q, k, v, lens = W.make_decode_inputs(w)
+    qd = torch.from_numpy(q).to(tdt).cuda()
+    sd = torch.from_numpy(lens).cuda()
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    if w.page_size:
+        kp, vp, table = W.build_pages(k, v, lens, w.page_size, w.seed)
+        kd, vd = (torch.from_numpy(x).to(tdt).cuda() for x in (kp, vp))
+        td = torch.from_numpy(table).cuda()
+        nk = w.page_size * table.shape[1]
+    else:
+        kd, vd = (torch.from_numpy(x).to(tdt).cuda() for x in (k, v))
+        nk = w.Nk
+    splits = args.splits if args.splits else fa._lib.fa_fwd_kvcache_num_splits(w.B, w.Hq, w.Hkv, w.Nq, nk)
+    ws_bytes = fa._lib.fa_fwd_kvcache_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, nk, w.d, splits)
+    ws = torch.empty(max(1, ws_bytes // 4), dtype=torch.float32, device="cuda")
+
+    if w.page_size:
+        def step():
+            fa.fwd_kvcache_paged(qd, kd, vd, td, sd, causal=w.causal, window_left=w.window_left, scale=w.scale,
+                                 num_splits=splits, out=o, lse=lse, workspace=ws, stream=stream)
+    else:
+        def step():
+            fa.fwd_kvcache(qd, kd, vd, sd, causal=w.causal, window_left=w.window_left, scale=w.scale,
+                           num_splits=splits, out=o, lse=lse, workspace=ws, stream=stream)
+
+    wall, per_call_ms = time_steps(step, args, name, stream)
+    avg_ms = float(np.mean(per_call_ms))
+    nbytes = W.decode_bytes(w, lens)
+    value = nbytes * args.steps / wall / 1e9
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    peak = 8000.0
+    rec = {
+        "metric": "attention decode GB/s + % of MI355X HBM bandwidth (8 TB/s)",
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "window_left": w.window_left, "page_size": w.page_size,
+                   "lengths": w.lengths, "total_keys": int(np.sum(lens)), "seed": w.seed, "splits": splits,
+                   "bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": peak, "unit": "GB/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "decode_split_kernel" + (" + decode_merge_kernel" if splits > 1 else ""),
+                     "avg_call_us": round(avg_ms * 1e3, 2),
+                     "min_call_us": round(float(np.min(per_call_ms)) * 1e3, 2)},
+    }
+    copy_note = calibration_copy(args.copy_calibration)
+    if copy_note:
+        rec["calibration"] = copy_note
+    if with_cpu:
+        print(f"[bench] {name}: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline_decode(w, q, k, v, lens)
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -357,6 +465,9 @@ def main():
                     help="also run a device copy of this size (counter calibration)")
     ap.add_argument("--bwd", action="store_true", help="time the backward pass instead of the forward")
     ap.add_argument("--fp8", action="store_true", help="time the FP8 forward (workload causal_8k_fp8)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time attention against a key/value cache (workload decode_gqa_32k, or --workload)")
+    ap.add_argument("--splits", type=int, default=None, help="--decode: split count (default: the library's)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the forward kernel runs on a single device "
@@ -368,6 +479,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     import workloads as W
+    if args.decode:
+        names = sorted(W.DECODE_WORKLOADS) if args.all else \
+            [args.workload if args.workload in W.DECODE_WORKLOADS else W.DECODE_HEADLINE]
+        for name in names:
+            print(json.dumps(run_decode(args, name, not args.all and not args.no_cpu_baseline)), flush=True)
+        return
     if args.fp8:
         name = args.workload if args.workload in W.FP8_WORKLOADS else "causal_8k_fp8"
         print(json.dumps(run_fp8(args, name, not args.no_cpu_baseline)), flush=True)

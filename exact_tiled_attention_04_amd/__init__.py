@@ -6,7 +6,9 @@ of ``include/fa.h``).  This package is a thin binding:
 
     _lib        the C entry points under their C names (raw addresses, sizes)
     attention   ``fwd(q, k, v, causal, window_left, scale)``,
-                ``fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, ...)`` and
+                ``fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, ...)``,
+                ``fwd_kvcache(q, k_cache, v_cache, cache_seqlens, ...)``,
+                ``fwd_kvcache_paged(q, k_pages, v_pages, block_table, ...)`` and
                 ``bwd(q, k, v, o, lse, dout, ...)`` on torch tensors
     build       compiles libfa.so in-tree with hipcc
 """
@@ -23,9 +25,19 @@ def fwd_fp8(*args, **kwargs):
     return _fwd_fp8(*args, **kwargs)
 
 
+def fwd_kvcache(*args, **kwargs):
+    from .attention import fwd_kvcache as _f
+    return _f(*args, **kwargs)
+
+
+def fwd_kvcache_paged(*args, **kwargs):
+    from .attention import fwd_kvcache_paged as _f
+    return _f(*args, **kwargs)
+
+
 def bwd(*args, **kwargs):
     from .attention import bwd as _bwd
     return _bwd(*args, **kwargs)
 
 
-__all__ = ["fwd", "fwd_fp8", "bwd", "FaError", "LIB_PATH", "load"]
+__all__ = ["fwd", "fwd_fp8", "fwd_kvcache", "fwd_kvcache_paged", "bwd", "FaError", "LIB_PATH", "load"]

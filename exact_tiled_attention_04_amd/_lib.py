@@ -22,8 +22,9 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_MISALIGNED = -3
 FA_ERR_HIP = -4
 
-EXPORTED = ["fa_fwd", "fa_fwd_bf16", "fa_fwd_f16", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_bwd_bf16", "fa_bwd_f16",
-            "fa_bwd_workspace_size", "fa_status_string", "fa_last_error", "fa_version"]
+EXPORTED = ["fa_fwd", "fa_fwd_bf16", "fa_fwd_f16", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_kvcache",
+            "fa_fwd_kvcache_paged", "fa_fwd_kvcache_num_splits", "fa_fwd_kvcache_workspace_size", "fa_bwd",
+            "fa_bwd_bf16", "fa_bwd_f16", "fa_bwd_workspace_size", "fa_status_string", "fa_last_error", "fa_version"]
 
 _lock = threading.Lock()
 _lib = None
@@ -57,6 +58,14 @@ def load() -> ctypes.CDLL:
         lib.fa_fwd.restype = I
         lib.fa_fwd_fp8.argtypes = [P, P, P, F, F, F, P, P, I, I, I, I, I, I, I, F, P]
         lib.fa_fwd_fp8.restype = I
+        lib.fa_fwd_kvcache.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, I]
+        lib.fa_fwd_kvcache.restype = I
+        lib.fa_fwd_kvcache_paged.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, P, I]
+        lib.fa_fwd_kvcache_paged.restype = I
+        lib.fa_fwd_kvcache_num_splits.argtypes = [I, I, I, I, I]
+        lib.fa_fwd_kvcache_num_splits.restype = I
+        lib.fa_fwd_kvcache_workspace_size.argtypes = [I, I, I, I, I, I, I]
+        lib.fa_fwd_kvcache_workspace_size.restype = ctypes.c_size_t
         bwd_args = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
         for name in ("fa_bwd_bf16", "fa_bwd_f16"):
             fn = getattr(lib, name)
@@ -104,6 +113,30 @@ def fa_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, d, cau
                stream) -> int:
     return load().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), q_scale, k_scale, v_scale, _ptr(o), _ptr(lse), B, Hq, Hkv,
                              N, d, int(bool(causal)), window_left, scale, _ptr(stream))
+
+
+def fa_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, o, lse, workspace, B, Hq, Hkv, Nq, Nk, d, causal,
+                   window_left, scale, num_splits, stream, dtype) -> int:
+    return load().fa_fwd_kvcache(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens), _ptr(o), _ptr(lse),
+                                 _ptr(workspace), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), window_left, scale,
+                                 num_splits, _ptr(stream), dtype)
+
+
+def fa_fwd_kvcache_paged(q, k_pages, v_pages, block_table, cache_seqlens, o, lse, workspace, B, Hq, Hkv, Nq, d,
+                         num_pages, page_size, max_pages_per_seq, causal, window_left, scale, num_splits, stream,
+                         dtype) -> int:
+    return load().fa_fwd_kvcache_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                       _ptr(cache_seqlens), _ptr(o), _ptr(lse), _ptr(workspace), B, Hq, Hkv, Nq, d,
+                                       num_pages, page_size, max_pages_per_seq, int(bool(causal)), window_left,
+                                       scale, num_splits, _ptr(stream), dtype)
+
+
+def fa_fwd_kvcache_num_splits(B: int, Hq: int, Hkv: int, Nq: int, Nk: int) -> int:
+    return load().fa_fwd_kvcache_num_splits(B, Hq, Hkv, Nq, Nk)
+
+
+def fa_fwd_kvcache_workspace_size(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, num_splits: int) -> int:
+    return load().fa_fwd_kvcache_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits)
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, causal, window_left, scale, stream,

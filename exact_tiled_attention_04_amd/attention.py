@@ -106,6 +106,111 @@ def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_scale: float, k
     return o, lse
 
 
+def _kv_common(q, k, v, out, lse, want_lse, workspace, B, Hq, Hkv, Nq, Nk, d, num_splits, stream):
+    if q.dtype not in (torch.float16, torch.bfloat16) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype, float16 or bfloat16")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on one GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    o = out if out is not None else torch.empty_like(q)
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, Hq, Nq) or lse.dtype != torch.float32
+                            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
+    nbytes = _lib.fa_fwd_kvcache_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
+    if workspace is not None and (workspace.dtype != torch.float32 or workspace.numel() * 4 < nbytes
+                                  or not workspace.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous float32 tensor of at least {nbytes} bytes")
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    return o, lse, workspace, s
+
+
+def _int32_dev(x, device, name):
+    if x is None:
+        return None
+    if not (isinstance(x, torch.Tensor) and x.dtype == torch.int32 and x.device == device and x.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous int32 tensor on the GPU of q")
+    return x
+
+
+def fwd_kvcache(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                cache_seqlens: Optional[torch.Tensor] = None, causal: bool = False, window_left: int = -1,
+                scale: Optional[float] = None, num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                workspace: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Attention of q [B, Hq, Nq, d] against a contiguous cache k_cache,
+    v_cache [B, Hkv, Nk, d] whose batch b holds cache_seqlens[b] keys (int32
+    on the GPU; None: all Nk).  Query rows stand at the end of the cache.
+    Returns (o like q, lse float32 [B, Hq, Nq]); rows that see no key get
+    o = 0, lse = -inf.  num_splits = 0 lets the library choose.  The split
+    workspace is allocated here unless given.  Asynchronous on ``stream``.
+    """
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B, Hq, Nq, d] and k_cache, v_cache [B, Hkv, Nk, d]")
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, dk = k_cache.shape
+    if k_cache.shape[0] != B or dk != d:
+        raise ValueError("k_cache, v_cache must be [B, Hkv, Nk, d] with q's B and d")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    seq = _int32_dev(cache_seqlens, q.device, "cache_seqlens")
+    o, lse, ws, s = _kv_common(q, k_cache, v_cache, out, lse, want_lse, workspace, B, Hq, Hkv, Nq, Nk, d,
+                               num_splits, stream)
+    with torch.cuda.device(q.device):
+        status = _lib.fa_fwd_kvcache(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                     seq.data_ptr() if seq is not None else None, o.data_ptr(),
+                                     lse.data_ptr() if lse is not None else None,
+                                     ws.data_ptr() if ws is not None else None, B, Hq, Hkv, Nq, Nk, d, causal,
+                                     window_left, float(scale), num_splits, s.cuda_stream, _DTYPES[q.dtype])
+    if status != _lib.FA_OK:
+        raise _lib.FaError(status, _lib.fa_last_error())
+    return o, lse
+
+
+def fwd_kvcache_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
+                      cache_seqlens: torch.Tensor, causal: bool = False, window_left: int = -1,
+                      scale: Optional[float] = None, num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                      lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                      workspace: Optional[torch.Tensor] = None,
+                      stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """As ``fwd_kvcache`` on a paged cache: k_pages, v_pages [num_pages,
+    page_size, Hkv, d]; block_table int32 [B, max_pages_per_seq] of page
+    indices; cache_seqlens int32 [B] (required)."""
+    if q.dim() != 4 or k_pages.dim() != 4 or k_pages.shape != v_pages.shape:
+        raise ValueError("q must be [B, Hq, Nq, d] and k_pages, v_pages [num_pages, page_size, Hkv, d]")
+    B, Hq, Nq, d = q.shape
+    num_pages, page_size, Hkv, dk = k_pages.shape
+    if dk != d:
+        raise ValueError("pages must have q's head dimension")
+    if block_table is None or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_pages_per_seq]")
+    if cache_seqlens is None or cache_seqlens.shape != (B,):
+        raise ValueError("cache_seqlens must be int32 [B]")
+    bt = _int32_dev(block_table, q.device, "block_table")
+    seq = _int32_dev(cache_seqlens, q.device, "cache_seqlens")
+    max_pages = bt.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o, lse, ws, s = _kv_common(q, k_pages, v_pages, out, lse, want_lse, workspace, B, Hq, Hkv, Nq,
+                               page_size * max_pages, d, num_splits, stream)
+    with torch.cuda.device(q.device):
+        status = _lib.fa_fwd_kvcache_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), bt.data_ptr(),
+                                           seq.data_ptr(), o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                           ws.data_ptr() if ws is not None else None, B, Hq, Hkv, Nq, d, num_pages,
+                                           page_size, max_pages, causal, window_left, float(scale), num_splits,
+                                           s.cuda_stream, _DTYPES[q.dtype])
+    if status != _lib.FA_OK:
+        raise _lib.FaError(status, _lib.fa_last_error())
+    return o, lse
+
+
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
         dout: torch.Tensor, causal: bool = False, window_left: int = -1, scale: Optional[float] = None,
         dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,

@@ -3,6 +3,7 @@
 // include/fa.h.
 #include "fa.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -10,6 +11,7 @@
 #include <cstring>
 
 #include "fa_internal.h"
+#include "fa_decode.h"
 
 namespace {
 
@@ -174,6 +176,138 @@ int run_fp8(const void* q, const void* k, const void* v, float q_scale, float k_
   return FA_OK;
 }
 
+// ---- key/value cache (decoding) ------------------------------------------
+
+// Splits of each (batch, key/value head, row block)'s key range when the
+// caller leaves the choice to the library: about four wavefronts per compute
+// unit (one round of the grid; more splits only add merge work and shorter
+// streams), at least four 32-key tiles per split, at most 128 splits.
+int auto_splits(long long base_items, int Nk) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  const long long target = 4LL * cus;
+  long long s = base_items > 0 ? (target + base_items - 1) / base_items : 1;
+  const long long max_s = std::max(1LL, ((long long)Nk + 32 * 4 - 1) / (32 * 4));
+  s = std::min(std::min(s, max_s), 128LL);
+  return (int)std::max(1LL, s);
+}
+
+int resolve_splits(int B, int Hq, int Hkv, int Nq, int Nk, int num_splits) {
+  if (num_splits > 0) return num_splits;
+  const long long rb = ((long long)(Hq / Hkv) * Nq + 31) / 32;
+  return auto_splits((long long)B * Hkv * rb, Nk);
+}
+
+uint64_t kvcache_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0 || Hq % Hkv != 0 || num_splits < 0) return 0;
+  const int s = resolve_splits(B, Hq, Hkv, Nq, Nk, num_splits);
+  return s <= 1 ? 0 : (uint64_t)s * B * Hq * Nq * (uint64_t)(d + 1) * sizeof(float);
+}
+
+int run_kvcache(const void* q, const void* k, const void* v, const int* block_table, const int* seqlens, void* o,
+                float* lse, float* workspace, int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_pages,
+                int page_size, int max_pages, int causal, int window_left, float scale, int num_splits,
+                void* stream, fa_dtype_t dtype, bool paged) {
+  g_last_error[0] = '\0';
+  if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "the key/value-cache path supports bf16 and fp16 only (dtype %d)",
+                static_cast<int>(dtype));
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0 || d < 0 || num_splits < 0)
+    return fail(FA_ERR_INVALID_ARG, "negative size (B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d splits=%d)", B, Hq, Hkv, Nq,
+                Nk, d, num_splits);
+  if (paged && (page_size <= 0 || max_pages <= 0 || num_pages <= 0))
+    return fail(FA_ERR_INVALID_ARG, "paged cache needs page_size, max_pages_per_seq and num_pages > 0");
+  if (B == 0 || Hq == 0 || Nq == 0) return FA_OK;
+  if (Hkv == 0 || Hq % Hkv != 0)
+    return fail(FA_ERR_INVALID_ARG, "Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
+  if (window_left < -1) return fail(FA_ERR_INVALID_ARG, "window_left=%d (must be -1 or >= 0)", window_left);
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale is not finite");
+  if (!(scale > 0.f)) return fail(FA_ERR_UNSUPPORTED, "scale=%g: only positive scales are supported", (double)scale);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d (supported: 64, 128)", d);
+  if (paged && page_size % 32 != 0)
+    return fail(FA_ERR_UNSUPPORTED, "page_size=%d must be a multiple of 32", page_size);
+  const long long cap = paged ? (long long)page_size * max_pages : (long long)Nk;
+  if (cap > INT32_MAX / 2) return fail(FA_ERR_UNSUPPORTED, "cache capacity of %lld keys is too large", cap);
+  if (!q || !k || !v || !o) return fail(FA_ERR_INVALID_ARG, "null q/k/v/o pointer");
+  if (paged && (!block_table || !seqlens))
+    return fail(FA_ERR_INVALID_ARG, "a paged cache needs block_table and cache_seqlens");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(FA_ERR_MISALIGNED, "q, k, v and o must be 16-byte aligned");
+  if ((lse && !aligned(lse, 4)) || (seqlens && !aligned(seqlens, 4)) || (block_table && !aligned(block_table, 4)))
+    return fail(FA_ERR_MISALIGNED, "lse, cache_seqlens and block_table must be 4-byte aligned");
+  // byte offsets inside one head (contiguous) or one page (paged) are 32-bit
+  const uint64_t span = paged ? (uint64_t)page_size * Hkv * d * 2 : (uint64_t)Nk * d * 2;
+  if (span + (1u << 20) > (uint64_t)INT32_MAX)
+    return fail(FA_ERR_UNSUPPORTED, paged ? "one page must stay below 2 GiB" : "one head's cache must stay below 2 GiB");
+  const int nk = (int)cap;
+  if (num_splits > 128) return fail(FA_ERR_UNSUPPORTED, "num_splits=%d (at most 128)", num_splits);
+  const int splits = resolve_splits(B, Hq, Hkv, Nq, nk, num_splits);
+  if (splits > 1 && !workspace)
+    return fail(FA_ERR_INVALID_ARG, "%d splits need a workspace (fa_fwd_kvcache_workspace_size bytes)", splits);
+  if (workspace && !aligned(workspace, 16)) return fail(FA_ERR_MISALIGNED, "the workspace must be 16-byte aligned");
+  const uint64_t n_q = (uint64_t)B * Hq * Nq * d * 2;
+  const uint64_t n_l = (uint64_t)B * Hq * Nq * sizeof(float);
+  const uint64_t n_kv = paged ? (uint64_t)num_pages * page_size * Hkv * d * 2 : (uint64_t)B * Hkv * Nk * d * 2;
+  const uint64_t n_w = kvcache_workspace_bytes(B, Hq, Hkv, Nq, nk, d, splits);
+  if (overlap(o, n_q, q, n_q) || overlap(o, n_q, k, n_kv) || overlap(o, n_q, v, n_kv))
+    return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
+  if (lse && (overlap(lse, n_l, o, n_q) || overlap(lse, n_l, q, n_q) || overlap(lse, n_l, k, n_kv) ||
+              overlap(lse, n_l, v, n_kv)))
+    return fail(FA_ERR_INVALID_ARG, "lse overlaps o or an input");
+  if (splits > 1 && (overlap(workspace, n_w, o, n_q) || overlap(workspace, n_w, q, n_q) ||
+                     (lse && overlap(workspace, n_w, lse, n_l)) || overlap(workspace, n_w, k, n_kv) ||
+                     overlap(workspace, n_w, v, n_kv)))
+    return fail(FA_ERR_INVALID_ARG, "the workspace overlaps another buffer");
+  const long long rb = ((long long)(Hq / Hkv) * Nq + 31) / 32;
+  const long long items = (long long)B * Hkv * rb * splits;
+  if (items > INT32_MAX / 2) return fail(FA_ERR_UNSUPPORTED, "B*Hkv*row blocks*splits=%lld is too many", items);
+
+  fa::DecodeParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.rows = (long long)B * Hq * Nq;
+  // workspace: partial outputs [splits][rows][d] (16-byte aligned rows), then
+  // partial logsumexps [splits][rows]
+  p.part_o = splits > 1 ? workspace : nullptr;
+  p.part_lse = splits > 1 ? workspace + (uint64_t)splits * p.rows * d : nullptr;
+  p.seqlens = seqlens;
+  p.block_table = paged ? block_table : nullptr;
+  p.row_stride = paged ? Hkv * d : d;
+  p.head_stride = paged ? d : (long long)Nk * d;
+  p.batch_stride = paged ? 0 : (long long)Hkv * Nk * d;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = Nq;
+  p.Nk = nk;
+  p.group = Hq / Hkv;
+  p.causal = causal ? 1 : 0;
+  // a window of Nk or more keys reaches past key 0 for every row
+  p.window_left = window_left >= nk ? -1 : window_left;
+  p.n_splits = splits;
+  {
+    // tiles a row block can need: the whole capacity, or its window plus rows
+    long long need = ((long long)nk + 31) / 32;
+    if (p.window_left >= 0) need = std::min(need, ((long long)p.window_left + Nq + 31) / 32 + 1);
+    p.tiles_per_split = (int)std::max(1LL, (need + splits - 1) / splits);
+  }
+  p.n_row_blocks = (int)rb;
+  p.total_items = (int)items;
+  p.page_size = paged ? page_size : 0;
+  p.max_pages = paged ? max_pages : 0;
+  p.num_pages = paged ? num_pages : 0;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const hipError_t e = fa::launch_decode(p, d, dtype == FA_DTYPE_F16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
 uint64_t bwd_workspace_bytes(int B, int Hq, int N) {
   return B <= 0 || Hq <= 0 || N <= 0 ? 0 : 2ull * (uint64_t)B * Hq * N * sizeof(float);
 }
@@ -271,6 +405,31 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float
   return run_fp8(q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, d, causal, window_left, scale, stream);
 }
 
+int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, const int* cache_seqlens, void* o,
+                   float* lse, float* workspace, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                   int window_left, float scale, int num_splits, void* stream, fa_dtype_t dtype) {
+  return run_kvcache(q, k_cache, v_cache, nullptr, cache_seqlens, o, lse, workspace, B, Hq, Hkv, Nq, Nk, d, 0, 0, 0,
+                     causal, window_left, scale, num_splits, stream, dtype, false);
+}
+
+int fa_fwd_kvcache_paged(const void* q, const void* k_pages, const void* v_pages, const int* block_table,
+                         const int* cache_seqlens, void* o, float* lse, float* workspace, int B, int Hq, int Hkv,
+                         int Nq, int d, int num_pages, int page_size, int max_pages_per_seq, int causal,
+                         int window_left, float scale, int num_splits, void* stream, fa_dtype_t dtype) {
+  return run_kvcache(q, k_pages, v_pages, block_table, cache_seqlens, o, lse, workspace, B, Hq, Hkv, Nq, 0, d,
+                     num_pages, page_size, max_pages_per_seq, causal, window_left, scale, num_splits, stream, dtype,
+                     true);
+}
+
+int fa_fwd_kvcache_num_splits(int B, int Hq, int Hkv, int Nq, int Nk) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || Hq % Hkv != 0) return 1;
+  return resolve_splits(B, Hq, Hkv, Nq, Nk, 0);
+}
+
+size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits) {
+  return (size_t)kvcache_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits);
+}
+
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
            void* dq, void* dk, void* dv, float* workspace, int B, int Hq, int Hkv, int N, int d, int causal,
            int window_left, float scale, void* stream, fa_dtype_t dtype) {
@@ -307,6 +466,6 @@ const char* fa_status_string(int status) {
 
 const char* fa_last_error(void) { return g_last_error; }
 
-int fa_version(void) { return 300; }  // 0.3.0
+int fa_version(void) { return 400; }  // 0.4.0
 
 }  // extern "C"

@@ -17,6 +17,8 @@ files under ``profiles/``.
 --kernel  substring selecting the kernel (default: the forward, "fwd_";
           "fwd_fp8" with --fp8 for the FP8 forward)
 --peak    TFLOP/s the algorithmic FLOPs are priced against (default 2516.6)
+--bytes   algorithmic bytes per launch, for HBM-bound kernels (priced
+          against 8000 GB/s)
 --name    output base name (default: fwd_<workload>; the traffic JSON that
           bench.py reads is written only for the forward)
 """
@@ -113,6 +115,8 @@ def main():
     ap.add_argument("--name", default=None)
     ap.add_argument("--flops", type=float, default=None, help="algorithmic FLOPs per launch")
     ap.add_argument("--peak", type=float, default=2516.6, help="peak TFLOP/s the FLOPs are priced against")
+    ap.add_argument("--bytes", type=float, default=None,
+                    help="algorithmic bytes per launch (HBM-bound kernels), priced against 8000 GB/s")
     ap.add_argument("--fp8", action="store_true", help="the FP8 forward kernel (its sources for the hash)")
     ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     args = ap.parse_args()
@@ -136,6 +140,10 @@ def main():
         lines.append(f"algorithmic FLOPs per launch {args.flops:.4e} -> {args.flops / (tr['avg_us'] * 1e-6) / 1e12:.1f} "
                      f"TFLOP/s at the average duration ({100 * args.flops / (tr['avg_us'] * 1e-6) / (args.peak * 1e12):.1f}% "
                      f"of {args.peak} TFLOP/s)")
+    if args.bytes:
+        gbs = args.bytes / (tr['avg_us'] * 1e-6) / 1e9
+        lines.append(f"algorithmic bytes per launch {args.bytes:.4e} -> {gbs:.1f} GB/s at the average duration "
+                     f"({100 * gbs / 8000:.1f}% of 8000 GB/s)")
     traffic = None
     if args.fetch and args.write and args.copy_mib:
         copy_bytes = args.copy_mib * 2 ** 20

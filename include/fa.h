@@ -144,6 +144,91 @@ int fa_fwd_fp8(const void *q, const void *k, const void *v,
                float scale, void *stream);
 
 /*
+ * Attention of a few query rows against a key/value cache (decoding).
+ *
+ * Batch b has a cache of L_b = cache_seqlens[b] keys (all Nk when
+ * cache_seqlens is NULL) and Nq query rows that stand at the end of it: row i
+ * is position L_b - Nq + i of the sequence.  For query head h (key/value head
+ * g(h) as in fa_fwd), row i and cached key j < L_b,
+ *
+ *     s_ij = scale * sum_c q[b][h][i][c] * k[b][g(h)][j][c]
+ *     (i, j) masked when (causal && j > L_b - Nq + i) or
+ *                        (window_left >= 0 && j < L_b - Nq + i - window_left)
+ *     o[b][h][i][:] = sum_j softmax_j(s_i.) v[b][g(h)][j][:],  lse = log sum_j exp(s_ij)
+ *
+ * i.e. the last Nq rows of fa_fwd over the whole sequence (the causal mask
+ * aligned to the end of the cache).  A row that sees no key (L_b < Nq - i
+ * under a causal mask, or L_b = 0) gets o = 0 and lse = -inf.  The pages
+ * name decoding and inference only in passing (the Hacker News thread, the
+ * FastAttention abstract); the alignment, the lengths and the empty-row
+ * values are this library's readings.
+ *
+ * The key range of each (batch, key/value head) is cut into num_splits parts
+ * processed in parallel; each writes a partial output and its logsumexp to
+ * the workspace, and a second kernel merges them (lse = log sum_s exp(lse_s),
+ * o = sum_s exp(lse_s - lse) o_s), the identity the tiling section of the
+ * Flash Attention page rests on.  num_splits = 0 lets the library choose
+ * (fa_fwd_kvcache_num_splits); with one split nothing goes through the
+ * workspace.  Results are deterministic for a given num_splits.
+ *
+ *   q             [B][Hq][Nq][d], element type dtype (FA_DTYPE_BF16 or F16).
+ *   k_cache, v_cache  [B][Hkv][Nk][d], same element type; keys at or past a
+ *                 batch's length are never read.
+ *   cache_seqlens device int32 [B] in [0, Nk] (values outside are clamped), or
+ *                 NULL for Nk everywhere.
+ *   o             [B][Hq][Nq][d] output, element type dtype.
+ *   lse           [B][Hq][Nq] float32 output (natural log), or NULL.
+ *   workspace     device memory of fa_fwd_kvcache_workspace_size(B, Hq, Hkv,
+ *                 Nq, Nk, d, num_splits) bytes, 16-byte aligned (NULL allowed
+ *                 when that size is 0); contents on entry ignored, on return
+ *                 unspecified.
+ *   B, Hq, Hkv, d, causal, window_left, scale, stream  as for fa_fwd.
+ *   Nq            query rows per sequence; Nk cache capacity in keys.
+ *   num_splits    0..128 (0: the library's choice).
+ *
+ * o, lse and the workspace must not overlap each other or any input.
+ * Errors as for fa_fwd, plus FA_ERR_UNSUPPORTED for FA_DTYPE_F32 and
+ * FA_ERR_INVALID_ARG for a missing workspace when more than one split runs.
+ */
+int fa_fwd_kvcache(const void *q, const void *k_cache, const void *v_cache,
+                   const int *cache_seqlens, void *o, float *lse, float *workspace,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                   int window_left, float scale, int num_splits, void *stream,
+                   fa_dtype_t dtype);
+
+/*
+ * The same operation on a paged cache: the keys of batch b are spread over
+ * fixed-size pages, key j living in page block_table[b][j / page_size] at
+ * slot j % page_size.
+ *
+ *   k_pages, v_pages  [num_pages][page_size][Hkv][d] (token-major pages).
+ *   block_table   device int32 [B][max_pages_per_seq] page indices; entries
+ *                 past a batch's length are not read; an index outside
+ *                 [0, num_pages) reads as zeros (never out of bounds).
+ *   cache_seqlens device int32 [B], required, in [0, page_size *
+ *                 max_pages_per_seq] (clamped).
+ *   page_size     a multiple of 32.
+ *   Everything else as fa_fwd_kvcache, with Nk = page_size * max_pages_per_seq
+ *   for the workspace size.
+ */
+int fa_fwd_kvcache_paged(const void *q, const void *k_pages, const void *v_pages,
+                         const int *block_table, const int *cache_seqlens, void *o,
+                         float *lse, float *workspace, int B, int Hq, int Hkv, int Nq,
+                         int d, int num_pages, int page_size, int max_pages_per_seq,
+                         int causal, int window_left, float scale, int num_splits,
+                         void *stream, fa_dtype_t dtype);
+
+/* Splits fa_fwd_kvcache uses when num_splits = 0 (enough parallel work for
+ * the current device, at least four 32-key tiles per split); 1 for sizes
+ * that compute nothing. */
+int fa_fwd_kvcache_num_splits(int B, int Hq, int Hkv, int Nq, int Nk);
+
+/* Workspace bytes fa_fwd_kvcache(_paged) needs for these sizes and
+ * num_splits (0 = the library's choice): splits * B * Hq * Nq * (d + 1) *
+ * sizeof(float) when more than one split runs, else 0. */
+size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
+
+/*
  * Gradients of fa_fwd's output with respect to q, k and v.
  *
  * For an upstream gradient dout = dL/do (the logsumexp output is taken to

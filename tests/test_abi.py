@@ -201,3 +201,74 @@ def test_fp8_validation_rejects(over, status):
 def test_fp8_empty_problem_is_a_noop():
     assert call_fp8(B=0, q=0, k=0, v=0, o=0, lse=0) == _lib.FA_OK
     assert call_fp8(N=0) == _lib.FA_OK
+
+
+# key/value cache: fake addresses; every case fails (or no-ops) before a launch
+SQ, BT, WS = 0xB00000, 0xC00000, 0xD00000
+GOOD_KV = dict(q=Q, k=K, v=V, seq=SQ, o=O, lse=L, ws=WS, B=1, Hq=4, Hkv=2, Nq=2, Nk=64, d=64, causal=1,
+               window_left=-1, scale=0.125, splits=2, stream=None)
+
+
+def call_kv(dtype=_lib.FA_DTYPE_BF16, **over):
+    a = dict(GOOD_KV, **over)
+    return _lib.fa_fwd_kvcache(a["q"], a["k"], a["v"], a["seq"], a["o"], a["lse"], a["ws"], a["B"], a["Hq"],
+                               a["Hkv"], a["Nq"], a["Nk"], a["d"], a["causal"], a["window_left"], a["scale"],
+                               a["splits"], a["stream"], dtype)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(B=-1), _lib.FA_ERR_INVALID_ARG),
+    (dict(Nk=-1), _lib.FA_ERR_INVALID_ARG),
+    (dict(splits=-1), _lib.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), _lib.FA_ERR_INVALID_ARG),
+    (dict(window_left=-2), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), _lib.FA_ERR_UNSUPPORTED),
+    (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
+    (dict(q=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(ws=0), _lib.FA_ERR_INVALID_ARG),                # two splits need a workspace
+    (dict(ws=WS + 4), _lib.FA_ERR_MISALIGNED),
+    (dict(seq=SQ + 2), _lib.FA_ERR_MISALIGNED),
+    (dict(o=Q), _lib.FA_ERR_INVALID_ARG),                 # output aliases q
+    (dict(ws=O + 64), _lib.FA_ERR_INVALID_ARG),           # workspace inside o
+    (dict(Nk=2 ** 30), _lib.FA_ERR_UNSUPPORTED),          # one head's cache beyond 2 GiB
+])
+def test_kvcache_validation_rejects(over, status):
+    assert call_kv(**over) == status
+    assert _lib.fa_last_error() != ""
+
+
+def test_kvcache_f32_and_empty():
+    assert call_kv(dtype=_lib.FA_DTYPE_F32) == _lib.FA_ERR_UNSUPPORTED
+    assert call_kv(B=0, q=0, k=0, v=0, o=0, lse=0, ws=0) == _lib.FA_OK
+    assert call_kv(Nq=0) == _lib.FA_OK
+
+
+def test_kvcache_paged_validation():
+    def call(**over):
+        a = dict(q=Q, k=K, v=V, bt=BT, seq=SQ, o=O, lse=L, ws=WS, B=1, Hq=4, Hkv=2, Nq=1, d=64, pages=8, ps=64,
+                 maxp=4, causal=1, wl=-1, scale=0.125, splits=2)
+        a.update(over)
+        return _lib.fa_fwd_kvcache_paged(a["q"], a["k"], a["v"], a["bt"], a["seq"], a["o"], a["lse"], a["ws"],
+                                         a["B"], a["Hq"], a["Hkv"], a["Nq"], a["d"], a["pages"], a["ps"], a["maxp"],
+                                         a["causal"], a["wl"], a["scale"], a["splits"], None, _lib.FA_DTYPE_BF16)
+    assert call(ps=48) == _lib.FA_ERR_UNSUPPORTED         # page size not a multiple of 32
+    assert call(ps=0) == _lib.FA_ERR_INVALID_ARG
+    assert call(pages=0) == _lib.FA_ERR_INVALID_ARG
+    assert call(bt=0) == _lib.FA_ERR_INVALID_ARG          # a paged cache needs its table
+    assert call(seq=0) == _lib.FA_ERR_INVALID_ARG         # and its lengths
+    assert call(bt=BT + 2) == _lib.FA_ERR_MISALIGNED
+    assert call(B=0) == _lib.FA_OK
+
+
+def test_kvcache_workspace_size():
+    ws = _lib.fa_fwd_kvcache_workspace_size
+    assert ws(2, 8, 2, 3, 1000, 128, 1) == 0
+    assert ws(2, 8, 2, 3, 1000, 128, 4) == 4 * 2 * 8 * 3 * 129 * 4
+    assert ws(0, 8, 2, 3, 1000, 128, 4) == 0
+    s = _lib.fa_fwd_kvcache_num_splits(2, 8, 2, 3, 1000)
+    assert 1 <= s <= 128
+    assert ws(2, 8, 2, 3, 1000, 128, 0) == (0 if s == 1 else s * 2 * 8 * 3 * 129 * 4)
+    # a short cache is never cut below four 32-key tiles per split
+    assert _lib.fa_fwd_kvcache_num_splits(1, 8, 8, 1, 100) == 1
+    assert _lib.fa_fwd_kvcache_num_splits(1, 8, 8, 1, 32768) >= 8

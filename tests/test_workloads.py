@@ -92,3 +92,40 @@ def test_fp8_quantisation_recipe():
     assert np.abs(qd - q32).max() <= 2 ** -4 * np.abs(q32).max() + 1e-12
     with pytest.raises(ValueError):
         W.round_to_fp8(np.array([500.0]))
+
+
+def test_decode_inputs_and_pages():
+    """Decoding inputs are seeded and exact in their type; paging scatters
+    every key of every sequence to the slot its table names, marks the rest,
+    and leaves nothing else behind."""
+    w = W.DECODE_WORKLOADS["decode_paged_varlen"].replace(B=3, Hq=4, Hkv=2, Nk=256, d=64)
+    q, k, v, lens = W.make_decode_inputs(w)
+    q2, _, _, lens2 = W.make_decode_inputs(w)
+    np.testing.assert_array_equal(q, q2)
+    np.testing.assert_array_equal(lens, lens2)
+    assert q.shape == (3, 4, 1, 64) and k.shape == (3, 2, 256, 64) and lens.dtype == np.int32
+    assert ((lens >= 1) & (lens <= 256)).all()
+    np.testing.assert_array_equal(W.round_to_bf16(k), k)
+    kp, vp, table = W.build_pages(k, v, lens, 64, w.seed, fill=np.nan, spare_pages=2)
+    assert kp.shape == (3 * 4 + 2, 64, 2, 64) and table.shape == (3, 4)
+    used = set()
+    for b in range(3):
+        L = int(lens[b])
+        for j in range(4):
+            if j * 64 >= L:
+                assert table[b, j] == -1
+                continue
+            page = table[b, j]
+            used.add(int(page))
+            for t in range(64):
+                key = j * 64 + t
+                if key < L:
+                    np.testing.assert_array_equal(kp[page, t], k[b, :, key])
+                    np.testing.assert_array_equal(vp[page, t], v[b, :, key])
+                else:
+                    assert np.isnan(kp[page, t]).all() and np.isnan(vp[page, t]).all()
+    for page in set(range(kp.shape[0])) - used:
+        assert np.isnan(kp[page]).all()
+    # full lengths by default
+    _, _, _, full = W.make_decode_inputs(W.DECODE_WORKLOADS["verify_16_16k"].replace(B=2, Nk=64, Hq=2, Hkv=1))
+    np.testing.assert_array_equal(full, [64, 64])

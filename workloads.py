@@ -218,6 +218,108 @@ def make_fp8_inputs(w: Workload, **over):
     return quantize_fp8(q), quantize_fp8(k), quantize_fp8(v)
 
 
+# ---------------------------------------------------------------------------
+# Decoding: Nq query rows per sequence against a key/value cache of per-batch
+# length (rows aligned to the end of the cache).  Same generator recipe:
+# Q, K, V standard normal in float32 over [B][Hq][Nq][d] and [B][Hkv][Nk][d],
+# then, for "uniform" lengths, B lengths drawn from integers(1, Nk + 1), then
+# rounding to the storage type.  A paged cache scatters the same keys into
+# pages of page_size slots in an order drawn from a generator seeded with
+# seed + 2000.
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    dtype: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    window_left: int
+    seed: int
+    lengths: str = "full"   # "full": every cache holds Nk keys; "uniform": lengths drawn in [1, Nk]
+    page_size: int = 0      # 0: contiguous cache [B][Hkv][Nk][d]; else pages [pages][page_size][Hkv][d]
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    def replace(self, **kw) -> "DecodeWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+DECODE_WORKLOADS = {
+    # one new token per sequence, GQA 4:1, 32k-token caches
+    "decode_gqa_32k": DecodeWorkload("decode_gqa_32k", "bf16", 8, 32, 8, 1, 32768, 128, True, -1, 5),
+    # one new token, mixed cache lengths up to 16k, paged in 64-token pages
+    "decode_paged_varlen": DecodeWorkload("decode_paged_varlen", "bf16", 16, 32, 8, 1, 16384, 128, True, -1, 6,
+                                          lengths="uniform", page_size=64),
+    # 16 new tokens per sequence (draft verification / chunked prefill) on 16k caches
+    "verify_16_16k": DecodeWorkload("verify_16_16k", "bf16", 4, 32, 8, 16, 16384, 128, True, -1, 7),
+}
+DECODE_HEADLINE = "decode_gqa_32k"
+
+
+def make_decode_inputs(w: DecodeWorkload, **over):
+    """(q, k, v, seqlens) for a decoding workload: q [B][Hq][Nq][d], k, v
+    [B][Hkv][Nk][d] float32 exact in w.dtype, seqlens int32 [B]."""
+    w = w.replace(**over) if over else w
+    rng = np.random.default_rng(w.seed)
+    q = rng.standard_normal((w.B, w.Hq, w.Nq, w.d), dtype=np.float32)
+    k = rng.standard_normal((w.B, w.Hkv, w.Nk, w.d), dtype=np.float32)
+    v = rng.standard_normal((w.B, w.Hkv, w.Nk, w.d), dtype=np.float32)
+    if w.lengths == "uniform":
+        seqlens = rng.integers(1, w.Nk + 1, w.B).astype(np.int32)
+    else:
+        seqlens = np.full(w.B, w.Nk, dtype=np.int32)
+    return round_to(w.dtype, q), round_to(w.dtype, k), round_to(w.dtype, v), seqlens
+
+
+def build_pages(k: np.ndarray, v: np.ndarray, seqlens, page_size: int, seed: int, fill: float = 0.0,
+                spare_pages: int = 0):
+    """Scatter a contiguous cache k, v [B][Hkv][Nk][d] into token-major pages
+    [num_pages][page_size][Hkv][d] in a seeded random page order.  Returns
+    (k_pages, v_pages, block_table int32 [B][max_pages]).  Slots past a
+    batch's length, pages no sequence uses (``spare_pages``) and table entries
+    past the length get ``fill`` (the table: -1), so that a reader that
+    touches them shows it."""
+    B, Hkv, Nk, d = k.shape
+    if page_size <= 0 or Nk % page_size:
+        raise ValueError("Nk must be a positive multiple of page_size")
+    max_pages = Nk // page_size
+    num_pages = B * max_pages + spare_pages
+    order = np.random.default_rng(seed + 2000).permutation(num_pages)
+    kp = np.full((num_pages, page_size, Hkv, d), fill, dtype=np.float32)
+    vp = np.full((num_pages, page_size, Hkv, d), fill, dtype=np.float32)
+    table = np.full((B, max_pages), -1, dtype=np.int32)
+    for b in range(B):
+        L = int(seqlens[b])
+        for j in range((L + page_size - 1) // page_size):
+            page = int(order[b * max_pages + j])
+            table[b, j] = page
+            n = min(page_size, L - j * page_size)
+            kp[page, :n] = k[b, :, j * page_size:j * page_size + n].transpose(1, 0, 2)
+            vp[page, :n] = v[b, :, j * page_size:j * page_size + n].transpose(1, 0, 2)
+    return kp, vp, table
+
+
+def decode_bytes(w: DecodeWorkload, seqlens, elem: int = 2) -> int:
+    """Bytes one decoding call must move at least: every visible cached key
+    and value row once per key/value head (the union over the group's query
+    rows), the query rows, and the output plus its logsumexp."""
+    kv = 0
+    for L in np.asarray(seqlens, dtype=np.int64):
+        L = int(L)
+        # union over the rows: the last row sees up to key L - 1 (with or
+        # without the causal mask), the first row's window starts lowest
+        lo = 0 if w.window_left < 0 else max(0, L - w.Nq - w.window_left)
+        kv += max(0, L - lo)
+    return (2 * kv * w.Hkv * w.d * elem + w.B * w.Hq * w.Nq * w.d * elem * 2 + w.B * w.Hq * w.Nq * 4)
+
+
 def unmasked_pairs(N: int, causal: bool, window_left: int) -> int:
     """Number of (query i, key j) pairs that a causal and/or left-window mask
     keeps, per head: key j is kept when j <= i (if causal) and j >= i - wl
