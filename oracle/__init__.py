@@ -16,7 +16,9 @@ Contents
                    partial output, one division at the end.
 ``attention_kvcache_ref``  the same attention for a few query rows against a
                    key/value cache of per-batch length (rows aligned to the
-                   end of the cache), as in decoding.
+                   end of the cache), as in decoding; and for a packed batch
+                   of sequences of different lengths (each sequence its own
+                   cache case).
 ``attention_bwd_ref``  fp64 gradients dQ, dK, dV of the forward above for an
                    upstream gradient dO (chain rule through O = P V and the
                    row softmax; P rebuilt per block of rows), with optional
@@ -53,4 +55,4 @@ from .attention_ref import attention_fwd, masked, kv_head_of  # noqa: F401
 from .twopass_ref import attention_twopass  # noqa: F401
 from .online_emul import attention_online  # noqa: F401
 from .attention_bwd_ref import attention_bwd  # noqa: F401
-from .attention_kvcache_ref import attention_fwd_kvcache  # noqa: F401
+from .attention_kvcache_ref import attention_fwd_kvcache, attention_fwd_varlen  # noqa: F401

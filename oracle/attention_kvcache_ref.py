@@ -110,3 +110,38 @@ def attention_fwd_kvcache(q, k, v, seqlens: Optional[Sequence[int]] = None, caus
         with ThreadPoolExecutor(nthreads) as ex:
             list(ex.map(work, range(n)))
     return o, lse
+
+
+def attention_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, causal: bool = False, window_left: int = -1,
+                         scale: Optional[float] = None, threads: Optional[int] = None):
+    """Attention over a batch of sequences of different lengths, packed.
+
+    q: [total_q, Hq, d]; k, v: [total_k, Hkv, d]; sequence b owns query rows
+    cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] ..
+    cu_seqlens_k[b+1]-1.  Each sequence is the cache case above with its own
+    Lq rows against its own Lk keys (rows aligned to the end of the keys; with
+    Lq = Lk this is ordinary self-attention).  Returns (o [total_q, Hq, d],
+    lse [Hq, total_q]); rows that see no key get o = 0, lse = -inf.
+    """
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = [int(x) for x in cu_seqlens_k]
+    if q.ndim != 3 or k.ndim != 3 or k.shape != v.shape or q.shape[2] != k.shape[2]:
+        raise ValueError("q must be [total_q, Hq, d] and k, v [total_k, Hkv, d]")
+    if len(cq) != len(ck) or len(cq) < 1 or cq[0] != 0 or ck[0] != 0 or cq[-1] != q.shape[0] \
+            or ck[-1] != k.shape[0] or any(b < a for a, b in zip(cq, cq[1:])) or any(b < a for a, b in zip(ck, ck[1:])):
+        raise ValueError("cu_seqlens must be nondecreasing prefix sums from 0 to the packed lengths")
+    Hq, d = q.shape[1], q.shape[2]
+    o = np.zeros((q.shape[0], Hq, d), dtype=np.float64)
+    lse = np.full((Hq, q.shape[0]), -np.inf, dtype=np.float64)
+    for b in range(len(cq) - 1):
+        q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if q1 == q0:
+            continue
+        qb = q[q0:q1].transpose(1, 0, 2)[None]          # [1, Hq, Lq, d]
+        kb = k[k0:k1].transpose(1, 0, 2)[None]          # [1, Hkv, Lk, d]
+        vb = v[k0:k1].transpose(1, 0, 2)[None]
+        ob, lb = attention_fwd_kvcache(qb, kb, vb, None, causal, window_left, scale, threads)
+        o[q0:q1] = ob[0].transpose(1, 0, 2)
+        lse[:, q0:q1] = lb[0]
+    return o, lse

@@ -79,3 +79,67 @@ def test_kv_pins_catch_planted_mistake(name, old, new):
         except (AssertionError, ValueError, IndexError, FloatingPointError):
             caught.append(pin.__name__)
     assert caught, f"no pin caught the planted mistake: {name}"
+
+
+# --- packed variable-length form ---------------------------------------------
+
+from oracle import attention_fwd, attention_fwd_varlen  # noqa: E402
+
+
+def _pack(x):
+    """[B, H, N, d] -> [B*N, H, d] (sequence-major packing)."""
+    B, H, N, d = x.shape
+    return np.ascontiguousarray(x.transpose(0, 2, 1, 3).reshape(B * N, H, d))
+
+
+def test_varlen_equal_lengths_equal_the_batched_forward():
+    """Packed sequences of one length give the batched forward oracle's
+    result (pinned on its own against torch)."""
+    rng = np.random.default_rng(920)
+    B, Hq, Hkv, N, d = 3, 4, 2, 37, 8
+    q, k, v = (rng.standard_normal(s) for s in [(B, Hq, N, d), (B, Hkv, N, d), (B, Hkv, N, d)])
+    cu = np.arange(B + 1) * N
+    for causal, wl in [(True, -1), (False, -1), (True, 5), (False, 3)]:
+        o, lse = attention_fwd_varlen(_pack(q), _pack(k), _pack(v), cu, cu, causal, wl, 0.3)
+        of, lf = attention_fwd(q, k, v, causal, wl, 0.3)
+        np.testing.assert_allclose(o, _pack(of), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, lf.transpose(1, 0, 2).reshape(Hq, B * N), rtol=0, atol=1e-12)
+
+
+def test_varlen_sequences_are_independent():
+    """Each packed sequence equals the forward oracle run on it alone (square
+    sequences), and a sequence with fewer queries than keys equals the last
+    rows of the forward over its keys; empty sequences contribute nothing."""
+    rng = np.random.default_rng(921)
+    Hq, Hkv, d = 4, 2, 8
+    lq = [5, 0, 12, 7, 1]
+    lk = [5, 0, 12, 19, 30]
+    cq, ck = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q = rng.standard_normal((cq[-1], Hq, d))
+    k = rng.standard_normal((ck[-1], Hkv, d))
+    v = rng.standard_normal((ck[-1], Hkv, d))
+    o, lse = attention_fwd_varlen(q, k, v, cq, ck, True, -1, 0.5)
+    for b in range(5):
+        if lq[b] == 0:
+            continue
+        L = lk[b]
+        early = rng.standard_normal((1, Hq, L - lq[b], d))
+        qf = np.concatenate([early, q[cq[b]:cq[b + 1]].transpose(1, 0, 2)[None]], axis=2)
+        of, lf = attention_fwd(qf, k[ck[b]:ck[b + 1]].transpose(1, 0, 2)[None],
+                               v[ck[b]:ck[b + 1]].transpose(1, 0, 2)[None], True, -1, 0.5)
+        np.testing.assert_allclose(o[cq[b]:cq[b + 1]], of[0, :, L - lq[b]:].transpose(1, 0, 2), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[:, cq[b]:cq[b + 1]], lf[0, :, L - lq[b]:], rtol=0, atol=1e-12)
+
+
+def test_varlen_more_queries_than_keys_and_bad_offsets():
+    rng = np.random.default_rng(922)
+    q = rng.standard_normal((6, 2, 4))
+    k = rng.standard_normal((2, 1, 4))
+    v = rng.standard_normal((2, 1, 4))
+    o, lse = attention_fwd_varlen(q, k, v, [0, 6], [0, 2], True, -1, 1.0)
+    assert (o[:4] == 0).all() and np.isneginf(lse[:, :4]).all()   # positions -4 .. -1 see nothing
+    np.testing.assert_allclose(o[4], np.repeat(v[0], 2, axis=0), rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        attention_fwd_varlen(q, k, v, [0, 5], [0, 2])
+    with pytest.raises(ValueError):
+        attention_fwd_varlen(q, k, v, [0, 4, 6], [0, 3, 2])
