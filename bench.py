@@ -2,7 +2,7 @@
 bf16/fp16 matrix-core peak.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload causal_8k]
-                    [--no-cpu-baseline] [--all] [--copy-calibration MiB] [--bwd] [--fp8] [--decode [--splits S]]
+                    [--no-cpu-baseline] [--all] [--copy-calibration MiB] [--bwd] [--fp8] [--decode [--splits S]] [--varlen]
 
 One step = one forward call (the whole path: Q/K/V tile staging, both
 contractions, online softmax, epilogue) over seeded synthetic inputs already
@@ -18,6 +18,10 @@ output) on the headline shape, against the dense fp8 matrix-core peak.
 ``--decode`` times attention against a key/value cache (few query rows per
 sequence, split-KV plus merge) on ``decode_gqa_32k`` (``--all``: every
 decoding workload), as algorithmic bytes per second against HBM bandwidth.
+
+``--varlen`` times the packed variable-length forward on
+``varlen_causal_16`` (16 sequences of 512-8192 tokens), FLOPs over the exact
+visible pairs of every sequence.
 
 ``--bwd`` times the backward instead (one step = one ``fa.bwd`` call: the
 row-term prep, dK/dV and dQ kernels) from the forward's o and lse, credited
@@ -449,6 +453,87 @@ def run_decode(args, name, with_cpu):
     return rec
 
 
+def cpu_baseline_varlen(w, q, k, v, cu, budget_s: float = 12.0):
+    """The fp64 packed oracle, as it stands, on a bounded sample: whole
+    sequences from the first, with every head and row, until ``budget_s`` of
+    wall time has passed (BLAS on one thread per worker)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import workloads as W
+    from oracle import attention_fwd_varlen
+
+    cores = len(os.sched_getaffinity(0))
+    done, flops = 0, 0.0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while done < w.B and time.perf_counter() - t0 < budget_s:
+            a, z = int(cu[done]), int(cu[done + 1])
+            sub = np.array([0, z - a], dtype=np.int32)
+            attention_fwd_varlen(q[a:z], k[a:z], v[a:z], sub, sub, w.causal, w.window_left, w.scale, threads=cores)
+            flops += W.varlen_metric_flops(w, sub)
+            done += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": min(cores, w.Hq), "kind": "oracle",
+            "sample": f"{done} of {w.B} sequences (every head and row), fp64 numpy, {dt:.1f} s wall"}
+
+
+def run_varlen(args, name, with_cpu):
+    """Packed sequences of different lengths: one step = one fa.fwd_varlen call."""
+    import numpy as np
+    import torch
+
+    import exact_tiled_attention_04_amd as fa
+    import workloads as W
+
+    w = W.VARLEN_WORKLOADS[name]
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    q, k, v, cu = W.make_varlen_inputs(w)
+    qd, kd, vd = (torch.from_numpy(x).to(tdt).cuda() for x in (q, k, v))
+    cud = torch.from_numpy(cu).cuda()
+    maxlen = int(np.diff(cu).max())
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.Hq, q.shape[0]), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fa.fwd_varlen(qd, kd, vd, cud, cud, maxlen, maxlen, causal=w.causal, window_left=w.window_left,
+                      scale=w.scale, out=o, lse=lse, stream=stream)
+
+    wall, per_launch_ms = time_steps(step, args, name, stream)
+    avg_ms = float(np.mean(per_launch_ms))
+    flops = W.varlen_metric_flops(w, cu)
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    rec = {
+        "metric": "attention fwd TFLOP/s + % of MI355X bf16 MFMA peak (packed sequences of different lengths)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "lengths": [int(x) for x in np.diff(cu)],
+                   "total_tokens": int(cu[-1]), "d": w.d, "causal": w.causal, "window_left": w.window_left,
+                   "scale": w.scale, "seed": w.seed, "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": "fwd_mfma_kernel (packed)",
+                     "avg_launch_us": round(avg_ms * 1e3, 2),
+                     "min_launch_us": round(float(np.min(per_launch_ms)) * 1e3, 2)},
+    }
+    if with_cpu:
+        print(f"[bench] {name}: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline_varlen(w, q, k, v, cu)
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -468,6 +553,8 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="time attention against a key/value cache (workload decode_gqa_32k, or --workload)")
     ap.add_argument("--splits", type=int, default=None, help="--decode: split count (default: the library's)")
+    ap.add_argument("--varlen", action="store_true",
+                    help="time the packed variable-length forward (workload varlen_causal_16)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the forward kernel runs on a single device "
@@ -479,6 +566,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     import workloads as W
+    if args.varlen:
+        name = args.workload if args.workload in W.VARLEN_WORKLOADS else "varlen_causal_16"
+        print(json.dumps(run_varlen(args, name, not args.no_cpu_baseline)), flush=True)
+        return
     if args.decode:
         names = sorted(W.DECODE_WORKLOADS) if args.all else \
             [args.workload if args.workload in W.DECODE_WORKLOADS else W.DECODE_HEADLINE]

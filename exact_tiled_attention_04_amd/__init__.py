@@ -6,6 +6,7 @@ of ``include/fa.h``).  This package is a thin binding:
 
     _lib        the C entry points under their C names (raw addresses, sizes)
     attention   ``fwd(q, k, v, causal, window_left, scale)``,
+                ``fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, ...)``,
                 ``fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, ...)``,
                 ``fwd_kvcache(q, k_cache, v_cache, cache_seqlens, ...)``,
                 ``fwd_kvcache_paged(q, k_pages, v_pages, block_table, ...)`` and
@@ -18,6 +19,11 @@ from ._lib import FaError, LIB_PATH, load  # noqa: F401
 def fwd(*args, **kwargs):
     from .attention import fwd as _fwd
     return _fwd(*args, **kwargs)
+
+
+def fwd_varlen(*args, **kwargs):
+    from .attention import fwd_varlen as _f
+    return _f(*args, **kwargs)
 
 
 def fwd_fp8(*args, **kwargs):
@@ -40,4 +46,4 @@ def bwd(*args, **kwargs):
     return _bwd(*args, **kwargs)
 
 
-__all__ = ["fwd", "fwd_fp8", "fwd_kvcache", "fwd_kvcache_paged", "bwd", "FaError", "LIB_PATH", "load"]
+__all__ = ["fwd", "fwd_varlen", "fwd_fp8", "fwd_kvcache", "fwd_kvcache_paged", "bwd", "FaError", "LIB_PATH", "load"]

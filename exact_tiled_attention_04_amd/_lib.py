@@ -22,7 +22,7 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_MISALIGNED = -3
 FA_ERR_HIP = -4
 
-EXPORTED = ["fa_fwd", "fa_fwd_bf16", "fa_fwd_f16", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_kvcache",
+EXPORTED = ["fa_fwd", "fa_fwd_bf16", "fa_fwd_f16", "fa_fwd_f32", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_kvcache",
             "fa_fwd_kvcache_paged", "fa_fwd_kvcache_num_splits", "fa_fwd_kvcache_workspace_size", "fa_bwd",
             "fa_bwd_bf16", "fa_bwd_f16", "fa_bwd_workspace_size", "fa_status_string", "fa_last_error", "fa_version"]
 
@@ -56,6 +56,8 @@ def load() -> ctypes.CDLL:
             fn.restype = I
         lib.fa_fwd.argtypes = fwd_args + [I]
         lib.fa_fwd.restype = I
+        lib.fa_fwd_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, P, I]
+        lib.fa_fwd_varlen.restype = I
         lib.fa_fwd_fp8.argtypes = [P, P, P, F, F, F, P, P, I, I, I, I, I, I, I, F, P]
         lib.fa_fwd_fp8.restype = I
         lib.fa_fwd_kvcache.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, I]
@@ -107,6 +109,13 @@ def fa_fwd_f16(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window_left, scale, st
 def fa_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window_left, scale, stream) -> int:
     return load().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
                              int(bool(causal)), window_left, scale, _ptr(stream))
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q, total_k, max_seqlen_q,
+                  max_seqlen_k, d, causal, window_left, scale, stream, dtype) -> int:
+    return load().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
+                                _ptr(cu_seqlens_k), B, Hq, Hkv, total_q, total_k, max_seqlen_q, max_seqlen_k, d,
+                                int(bool(causal)), window_left, scale, _ptr(stream), dtype)
 
 
 def fa_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, d, causal, window_left, scale,

@@ -58,6 +58,53 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     return o, lse
 
 
+def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+               cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, causal: bool = False,
+               window_left: int = -1, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+               stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Attention over packed sequences of different lengths: q [total_q, Hq,
+    d], k, v [total_k, Hkv, d] (float16 or bfloat16, contiguous), cu_seqlens_q
+    and cu_seqlens_k int32 [B+1] offsets on the GPU, max_seqlen_q and
+    max_seqlen_k the longest lengths.  Each sequence's query rows stand at the
+    end of its keys.  Returns (o like q, lse float32 [Hq, total_q]).
+    Asynchronous on ``stream``."""
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or k.shape[2] != q.shape[2]:
+        raise ValueError("q must be [total_q, Hq, d] and k, v [total_k, Hkv, d]")
+    if q.dtype not in (torch.float16, torch.bfloat16) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype, float16 or bfloat16")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on one GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    cq = _int32_dev(cu_seqlens_q, q.device, "cu_seqlens_q")
+    ck = _int32_dev(cu_seqlens_k, q.device, "cu_seqlens_k")
+    if cq is None or ck is None or cq.dim() != 1 or cq.shape != ck.shape or cq.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be int32 [B+1]")
+    total_q, Hq, d = q.shape
+    total_k, Hkv, _ = k.shape
+    B = cq.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = out if out is not None else torch.empty_like(q)
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None and want_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (Hq, total_q) or lse.dtype != torch.float32
+                            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [Hq, total_q] tensor")
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        status = _lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    lse.data_ptr() if lse is not None else None, cq.data_ptr(), ck.data_ptr(),
+                                    B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), d, causal,
+                                    window_left, float(scale), s.cuda_stream, _DTYPES[q.dtype])
+    if status != _lib.FA_OK:
+        raise _lib.FaError(status, _lib.fa_last_error())
+    return o, lse
+
+
 _BYTE_TYPES = (torch.uint8, torch.float8_e4m3fn)
 
 

@@ -120,6 +120,68 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   return FA_OK;
 }
 
+int run_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_q, const int* cu_k,
+               int B, int Hq, int Hkv, int total_q, int total_k, int max_q, int max_k, int d, int causal,
+               int window_left, float scale, void* stream, fa_dtype_t dtype) {
+  g_last_error[0] = '\0';
+  if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "packed sequences support bf16 and fp16 only (dtype %d)", static_cast<int>(dtype));
+  if (B < 0 || Hq < 0 || Hkv < 0 || total_q < 0 || total_k < 0 || max_q < 0 || max_k < 0 || d < 0)
+    return fail(FA_ERR_INVALID_ARG, "negative size (B=%d Hq=%d Hkv=%d total_q=%d total_k=%d max_q=%d max_k=%d d=%d)",
+                B, Hq, Hkv, total_q, total_k, max_q, max_k, d);
+  if (B == 0 || Hq == 0 || total_q == 0 || max_q == 0) return FA_OK;
+  if (Hkv == 0 || Hq % Hkv != 0)
+    return fail(FA_ERR_INVALID_ARG, "Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
+  if (window_left < -1) return fail(FA_ERR_INVALID_ARG, "window_left=%d (must be -1 or >= 0)", window_left);
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale is not finite");
+  if (!(scale > 0.f)) return fail(FA_ERR_UNSUPPORTED, "scale=%g: only positive scales are supported", (double)scale);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d (supported: 64, 128)", d);
+  if (!q || !k || !v || !o || !cu_q || !cu_k)
+    return fail(FA_ERR_INVALID_ARG, "null q/k/v/o/cu_seqlens pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(FA_ERR_MISALIGNED, "q, k, v and o must be 16-byte aligned");
+  if ((lse && !aligned(lse, 4)) || !aligned(cu_q, 4) || !aligned(cu_k, 4))
+    return fail(FA_ERR_MISALIGNED, "lse and cu_seqlens must be 4-byte aligned");
+  const uint64_t n_q = (uint64_t)total_q * Hq * d * 2;
+  const uint64_t n_kv = (uint64_t)total_k * Hkv * d * 2;
+  const uint64_t n_l = (uint64_t)Hq * total_q * sizeof(float);
+  if (overlap(o, n_q, q, n_q) || overlap(o, n_q, k, n_kv) || overlap(o, n_q, v, n_kv))
+    return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
+  if (lse && (overlap(lse, n_l, o, n_q) || overlap(lse, n_l, q, n_q) || overlap(lse, n_l, k, n_kv) ||
+              overlap(lse, n_l, v, n_kv)))
+    return fail(FA_ERR_INVALID_ARG, "lse overlaps o or an input");
+  // one sequence's keys of one head are addressed with 32-bit byte offsets
+  if ((uint64_t)max_k * Hkv * d * 2 + (1u << 20) > (uint64_t)INT32_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "max_seqlen_k=%d too long (one sequence's keys must stay below 2 GiB)", max_k);
+  const long long rows = fa::mfma_rows_per_workgroup();
+  // the launch rounds the (sequence, key/value head) groups up to a multiple of 8
+  const long long items = 8 * (((long long)B * Hkv + 7) / 8) * (Hq / Hkv) * ((max_q + rows - 1) / rows);
+  if (items > fa::kMaxGridItems) return fail(FA_ERR_UNSUPPORTED, "B*Hq*ceil(max_seqlen_q/%lld) too large", rows);
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.N = max_q;
+  a.d = d;
+  a.causal = causal;
+  a.window_left = window_left;
+  a.scale = scale;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  a.max_k = max_k;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f16(a, s);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
 int run_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale, float v_scale, void* o,
             float* lse, int B, int Hq, int Hkv, int N, int d, int causal, int window_left, float scale,
             void* stream) {
@@ -399,6 +461,14 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
   return run(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window_left, scale, stream, FA_DTYPE_F32);
 }
 
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens_q,
+                  const int* cu_seqlens_k, int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                  int max_seqlen_k, int d, int causal, int window_left, float scale, void* stream,
+                  fa_dtype_t dtype) {
+  return run_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q, total_k, max_seqlen_q,
+                    max_seqlen_k, d, causal, window_left, scale, stream, dtype);
+}
+
 int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale, float v_scale, void* o,
                float* lse, int B, int Hq, int Hkv, int N, int d, int causal, int window_left, float scale,
                void* stream) {
@@ -466,6 +536,6 @@ const char* fa_status_string(int status) {
 
 const char* fa_last_error(void) { return g_last_error; }
 
-int fa_version(void) { return 400; }  // 0.4.0
+int fa_version(void) { return 500; }  // 0.5.0
 
 }  // extern "C"

@@ -43,6 +43,7 @@
 #include "fa_internal.h"
 #include "fa_mfma_common.h"
 
+#include <climits>
 #include <type_traits>
 
 namespace fa {
@@ -119,15 +120,17 @@ template <int D>
 struct LoadOffsets {
   int k[Shape<D>::kLoadsPerWave];
   int v[Shape<D>::kLoadsPerWave];
-  __device__ __forceinline__ void init(int wave, int lane) {
+  // row_bytes: distance between consecutive keys of one head in device
+  // memory (2d for [B][H][N][d]; 2 * Hkv * d for packed [tokens][Hkv][d])
+  __device__ __forceinline__ void init(int wave, int lane, int row_bytes) {
     using S = Shape<D>;
 #pragma unroll
     for (int u = 0; u < S::kLoadsPerWave; ++u) {
       const int piece = wave * S::kLoadsPerWave + u;
       const int row = piece * S::kRowsPerLoad + lane / S::kChunks;
       const int pch = lane % S::kChunks;  // physical chunk this lane fills
-      k[u] = row * S::kRowBytes + ((pch ^ k_swz<D>(row)) << 4);
-      v[u] = row * S::kRowBytes + ((pch ^ v_swz<D>(row)) << 4);
+      k[u] = row * row_bytes + ((pch ^ k_swz<D>(row)) << 4);
+      v[u] = row * row_bytes + ((pch ^ v_swz<D>(row)) << 4);
     }
   }
 };
@@ -138,9 +141,9 @@ struct LoadOffsets {
 // outside the buffer's range and arrive as zeros.
 template <int D>
 __device__ __forceinline__ void copy_tile_async(__amdgpu_buffer_rsrc_t r, const int* lane_off,
-                                                unsigned short* dst, int t, int wave) {
+                                                unsigned short* dst, int t, int wave, int row_bytes) {
   using S = Shape<D>;
-  const int tile_bytes = t * (kBC * S::kRowBytes);
+  const int tile_bytes = t * (kBC * row_bytes);
 #pragma unroll
   for (int u = 0; u < S::kLoadsPerWave; ++u) {
     const int piece = wave * S::kLoadsPerWave + u;
@@ -165,6 +168,8 @@ struct LoopCtx {
   int N, wl, t_beg, t_end;
   int wave, lane, l32, hh;
   int wq0, wq1;                   // first and last valid row of the wavefront
+  int shift;                      // key position of query row 0 (0 unless fewer queries than keys)
+  int kv_row_bytes;               // distance between consecutive keys of one head
   int vis_lo;                     // first visible key of this lane's row
   unsigned vis_span;              // visible keys: vis_lo .. vis_lo + vis_span
   int v_row_lane, v_col_lane;     // lane geometry of the transposing V read
@@ -204,7 +209,8 @@ template <int D>
 __device__ __forceinline__ void tile_mask(const LoopCtx<D>& x, int t, f32x16 (&s)[kHalves]) {
   const int kb = t * kBC;
   const int ke = kb + kBC - 1;
-  const bool need_mask = (ke >= x.N) || (x.causal && ke > x.wq0) || (x.wl >= 0 && kb < x.wq1 - x.wl);
+  const bool need_mask = (ke >= x.N) || (x.causal && ke > x.wq0 + x.shift) ||
+                         (x.wl >= 0 && kb < x.wq1 + x.shift - x.wl);
   if (!need_mask) return;
   const int base = kb - x.vis_lo + 4 * x.hh;
 #pragma unroll
@@ -334,8 +340,8 @@ __device__ __forceinline__ void pipeline_step(const unsigned short* __restrict__
                                               float& alpha_prev, int t) {
   using S = Shape<D>;
   // V(t) (two V buffers) or V(t+1) (three); past the end: zeros, never read
-  copy_tile_async<D>(x.rv, x.off.v, vN, t + kVBufs - 2, x.wave);
-  copy_tile_async<D>(x.rk, x.off.k, kN, t + 2, x.wave);
+  copy_tile_async<D>(x.rv, x.off.v, vN, t + kVBufs - 2, x.wave, x.kv_row_bytes);
+  copy_tile_async<D>(x.rk, x.off.k, kN, t + 2, x.wave, x.kv_row_bytes);
 
   f32x16 s[kHalves];
   __builtin_amdgcn_s_setprio(2);
@@ -378,7 +384,13 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kInFlight) : "memory");
 }
 
-template <typename E, int D>
+// kVarlen: sequences of different lengths packed as q [total_q][Hq][d],
+// k, v [total_k][Hkv][d], sequence b owning rows cu_q[b] .. cu_q[b+1]-1 (and
+// keys cu_k[b] .. cu_k[b+1]-1); its Lq query rows stand at the end of its Lk
+// keys (row i at position Lk - Lq + i), lse is [Hq][total_q], and rows that
+// see no key get o = 0 and lse = -inf.  Otherwise one N for queries and keys
+// in [B][H][N][d].
+template <typename E, int D, bool kVarlen>
 __global__ void __launch_bounds__(kThreads, kWavesPerSimd) fwd_mfma_kernel(FwdParams p) {
   using S = Shape<D>;
   // three K and two V buffers, as separate objects (80 KiB at d = 128, so two
@@ -400,18 +412,67 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) fwd_mfma_kernel(FwdPa
   x.wave = __builtin_amdgcn_readfirstlane(tid / kWaveSize);  // wave-uniform: keep it scalar
   x.l32 = x.lane & 31;
   x.hh = x.lane >> 5;
-  x.off.init(x.wave, x.lane);
 
-  const WorkItem it = decode_work_item(p, blockIdx.x);
-  const int N = p.N;
-  x.N = N;
+  WorkItem it;
+  if constexpr (kVarlen) {
+    // Packed sequences of different lengths cost very different amounts, so
+    // instead of contiguous slices of the (sequence, key/value head) groups,
+    // XCD x (workgroup id mod 8) takes groups x, x + 8, x + 16, ...: every
+    // XCD gets a spread of lengths.  A group's query blocks (and the query
+    // heads sharing its key/value head) stay on one XCD, heaviest block
+    // first, so its K/V tiles are shared through that XCD's L2.  The grid
+    // holds 8 * ceil(groups / 8) groups; the missing ones return at once.
+    const int xcd = blockIdx.x % 8;
+    const int r = blockIdx.x / 8;
+    const int per_group = p.group * p.n_qblocks;
+    const int j = r / per_group;
+    const int w = r - j * per_group;
+    const int gidx = 8 * j + xcd;
+    if (gidx >= p.B * p.Hkv) return;
+    const int qrank = w / p.group;
+    const int hg = w - qrank * p.group;
+    const int gb = gidx / p.Hkv;
+    it.bh = gb * p.Hq + (gidx - gb * p.Hkv) * p.group + hg;
+    it.qb = p.causal ? (p.n_qblocks - 1 - qrank) : qrank;
+  } else {
+    it = decode_work_item(p, blockIdx.x);
+  }
   const int b = it.bh / p.Hq;
   const int hq = it.bh - b * p.Hq;
   const int hk = hq / p.group;
-  const long long q_head = (long long)it.bh * N * D;
-  const long long kv_head = ((long long)b * p.Hkv + hk) * N * D;
+  int Nq, N;                // query rows and keys of this sequence
+  long long q_head, kv_head;  // element offsets of this head's row 0
+  int q_stride;             // elements between consecutive query rows
+  int q_row0 = 0;           // packed: the sequence's first row in q
+  if constexpr (kVarlen) {
+    // offsets clamped to the packed tensors, lengths to the launch's maxima,
+    // so inconsistent offsets can never address outside the buffers
+    typedef __attribute__((address_space(4))) const int cint;
+    const int qa = min(max(((cint*)p.cu_q)[b], 0), p.total_q);
+    const int qz = min(max(((cint*)p.cu_q)[b + 1], qa), p.total_q);
+    const int ka = min(max(((cint*)p.cu_k)[b], 0), p.total_k);
+    const int kz = min(max(((cint*)p.cu_k)[b + 1], ka), p.total_k);
+    Nq = min(qz - qa, p.N);
+    N = min(kz - ka, p.max_k);
+    if (it.qb * kBR >= Nq) return;  // the whole workgroup: past this sequence's rows
+    x.shift = N - Nq;
+    q_row0 = qa;
+    q_head = ((long long)qa * p.Hq + hq) * D;
+    kv_head = ((long long)ka * p.Hkv + hk) * D;
+    q_stride = p.Hq * D;
+    x.kv_row_bytes = 2 * p.Hkv * D;
+  } else {
+    Nq = N = p.N;
+    x.shift = 0;
+    q_head = (long long)it.bh * N * D;
+    kv_head = ((long long)b * p.Hkv + hk) * N * D;
+    q_stride = D;
+    x.kv_row_bytes = S::kRowBytes;
+  }
+  x.off.init(x.wave, x.lane, x.kv_row_bytes);
+  x.N = N;
   const unsigned short* __restrict__ qg = (const unsigned short*)p.q + q_head;
-  const int head_bytes = N * S::kRowBytes;
+  const int head_bytes = kVarlen ? (N > 0 ? (N - 1) * x.kv_row_bytes + S::kRowBytes : 0) : N * S::kRowBytes;
   x.rk = __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned short*)p.k + kv_head), 0, head_bytes,
                                            kBufferFlags);
   x.rv = __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned short*)p.v + kv_head), 0, head_bytes,
@@ -422,20 +483,36 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) fwd_mfma_kernel(FwdPa
   x.c = p.scale_log2;
   const int q0 = it.qb * kBR;
   x.wq0 = q0 + x.wave * kRowsPerWave;
-  x.wq1 = min(N, x.wq0 + kRowsPerWave) - 1;
+  x.wq1 = min(Nq, x.wq0 + kRowsPerWave) - 1;
   const int myq = x.wq0 + x.l32;  // this lane's query row
 
   // Key tiles this workgroup needs: causal stops at its last row, a window
   // starts window_left keys before its first row.
-  const int kend = x.causal ? min(N, q0 + kBR) : N;
-  const int kbeg = x.wl >= 0 ? max(0, q0 - x.wl) : 0;
+  const int kend = x.causal ? min(N, q0 + kBR + x.shift) : N;
+  const int kbeg = x.wl >= 0 ? max(0, q0 + x.shift - x.wl) : 0;
   x.t_beg = kbeg / kBC;
   x.t_end = (kend + kBC - 1) / kBC;
 
   // Visible keys of this lane's row form one range [vis_lo, vis_lo + vis_span].
-  x.vis_lo = x.wl >= 0 ? max(0, myq - x.wl) : 0;
-  const int vis_hi = x.causal ? min(myq, N - 1) : N - 1;
+  const int pos = myq + x.shift;
+  x.vis_lo = x.wl >= 0 ? max(0, pos - x.wl) : 0;
+  const int vis_hi = x.causal ? min(pos, N - 1) : N - 1;
   x.vis_span = (unsigned)(vis_hi - x.vis_lo);
+  if constexpr (kVarlen) {
+    if (vis_hi < x.vis_lo) {  // a row that sees no key: nothing is visible
+      x.vis_lo = INT_MAX / 2;
+      x.vis_span = 0;
+    }
+    if (kend <= kbeg) {  // no row of the workgroup sees a key
+      if (myq < Nq) {
+        unsigned short* og = (unsigned short*)p.o + q_head + (long long)myq * q_stride;
+#pragma unroll
+        for (int c = 0; c < D / 4; c += 2) *(u32x2*)(og + 4 * (c + x.hh)) = u32x2{0u, 0u};
+        if (x.hh == 0 && p.lse != nullptr) p.lse[(long long)hq * p.total_q + q_row0 + myq] = -INFINITY;
+      }
+      return;
+    }
+  }
 
   const int g16 = x.lane >> 4;
   const int gi = x.lane & 15;
@@ -445,8 +522,8 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) fwd_mfma_kernel(FwdPa
   RowState<D> st;
 #pragma unroll
   for (int kc = 0; kc < S::kSteps; ++kc) {
-    if (myq < N)
-      st.qf[kc] = *(const u32x4*)(qg + (long long)myq * D + 16 * kc + 8 * x.hh);
+    if (myq < Nq)
+      st.qf[kc] = *(const u32x4*)(qg + (long long)myq * q_stride + 16 * kc + 8 * x.hh);
     else
       st.qf[kc] = u32x4{0u, 0u, 0u, 0u};
   }
@@ -466,9 +543,9 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) fwd_mfma_kernel(FwdPa
   // previous step's copies
   constexpr int kInFlight = (kVBufs - 1) * S::kLoadsPerWave;
   const int t0 = x.t_beg;
-  copy_tile_async<D>(x.rk, x.off.k, sK0, t0, x.wave);
-  copy_tile_async<D>(x.rk, x.off.k, sK1, t0 + 1, x.wave);  // past the end: zeros, never read
-  if (kVBufs == 3) copy_tile_async<D>(x.rv, x.off.v, sV0, t0, x.wave);
+  copy_tile_async<D>(x.rk, x.off.k, sK0, t0, x.wave, x.kv_row_bytes);
+  copy_tile_async<D>(x.rk, x.off.k, sK1, t0 + 1, x.wave, x.kv_row_bytes);  // past the end: zeros, never read
+  if (kVBufs == 3) copy_tile_async<D>(x.rv, x.off.v, sV0, t0, x.wave, x.kv_row_bytes);
   u32x4 pf_prev[2 * kHalves];
   float alpha_prev = 1.f;
   tile_barrier<0>();
@@ -507,9 +584,10 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) fwd_mfma_kernel(FwdPa
   float llo, lhi;
   half_pair(st.l_run, llo, lhi);
   const float l_tot = llo + lhi;
-  if (myq < N) {
-    const float inv = 1.f / l_tot;
-    unsigned short* og = (unsigned short*)p.o + q_head + (long long)myq * D;
+  if (myq < Nq) {
+    const bool seen = !kVarlen || l_tot > 0.f;  // only packed rows can see no key
+    const float inv = seen ? 1.f / l_tot : 0.f;
+    unsigned short* og = (unsigned short*)p.o + q_head + (long long)myq * q_stride;
 #pragma unroll
     for (int ct = 0; ct < S::kOutTiles; ++ct) {
 #pragma unroll
@@ -519,15 +597,27 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) fwd_mfma_kernel(FwdPa
         *(u32x2*)(og + 32 * ct + 8 * gq + 4 * x.hh) = w;
       }
     }
-    if (x.hh == 0 && p.lse != nullptr)
-      p.lse[(long long)it.bh * N + myq] = (st.m_use + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    if (x.hh == 0 && p.lse != nullptr) {
+      const float lse = seen ? (st.m_use + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+      if constexpr (kVarlen)
+        p.lse[(long long)hq * p.total_q + q_row0 + myq] = lse;
+      else
+        p.lse[(long long)it.bh * N + myq] = lse;
+    }
   }
 }
 
 template <typename E, int D>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const FwdParams p = make_params(a, kBR);
-  hipLaunchKernelGGL((fwd_mfma_kernel<E, D>), dim3(p.total_items), dim3(kThreads), 0, stream, p);
+  if (p.cu_q) {
+    // eight XCDs times the rounds of (sequence, key/value head) groups
+    const long long groups = (long long)p.B * p.Hkv;
+    const long long grid = 8 * ((groups + 7) / 8) * p.group * p.n_qblocks;
+    hipLaunchKernelGGL((fwd_mfma_kernel<E, D, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((fwd_mfma_kernel<E, D, false>), dim3(p.total_items), dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -17,6 +17,13 @@ struct FwdArgs {
   int causal;
   int window_left;  // -1 = no window
   float scale;      // > 0
+  // packed sequences of different lengths (null: one N for all): q [total_q]
+  // [Hq][d], k, v [total_k][Hkv][d], sequence b owning rows cu_q[b] ..
+  // cu_q[b+1]-1 and keys cu_k[b] .. cu_k[b+1]-1; N is then the longest query
+  // count and max_k the longest key count
+  const int* cu_q = nullptr;
+  const int* cu_k = nullptr;
+  int total_q = 0, total_k = 0, max_k = 0;
 };
 
 // Kernel-side copy of the arguments plus derived constants.
@@ -35,6 +42,9 @@ struct FwdParams {
   float scale_log2;  // scale * log2(e): scores go straight into exp2
                      // (FP8: times the Q and K scales)
   float o_mult;      // multiplier on the output: the V scale of FP8 inputs, else 1
+  const int* cu_q;   // packed variable-length sequences (null: fixed N), as FwdArgs
+  const int* cu_k;
+  int total_q, total_k, max_k;
 };
 
 // Workgroup -> (batch*head, query block) mapping.
@@ -91,11 +101,18 @@ inline FwdParams make_params(const FwdArgs& a, int rows_per_wg) {
   p.group = a.Hq / a.Hkv;
   p.causal = a.causal ? 1 : 0;
   // a window of N-1 or more keys reaches back past key 0 and hides nothing
-  p.window_left = (a.window_left >= a.N - 1) ? -1 : a.window_left;
+  // (packed sequences: of the longest key count - 1 or more)
+  const int span = a.cu_q ? (a.N > a.max_k ? a.N : a.max_k) : a.N;
+  p.window_left = (a.window_left >= span - 1) ? -1 : a.window_left;
   p.n_qblocks = (a.N + rows_per_wg - 1) / rows_per_wg;
   p.total_items = a.B * a.Hq * p.n_qblocks;
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.o_mult = 1.f;
+  p.cu_q = a.cu_q;
+  p.cu_k = a.cu_k;
+  p.total_q = a.total_q;
+  p.total_k = a.total_k;
+  p.max_k = a.max_k;
   return p;
 }
 

@@ -107,6 +107,39 @@ int fa_fwd_f32(const void *q, const void *k, const void *v, void *o, float *lse,
                float scale, void *stream);
 
 /*
+ * Attention forward over a batch of sequences of different lengths, packed.
+ *
+ * Sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q and
+ * key/value rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k and v; with
+ * Lq = cu_seqlens_q[b+1] - cu_seqlens_q[b] and Lk likewise, its query row i
+ * stands at key position Lk - Lq + i (equal lengths: ordinary self-attention,
+ * fewer queries than keys: the queries are the sequence's last tokens), and
+ * the operation is fa_fwd's within each sequence, the causal mask and window
+ * measured from that position.  Rows that see no key (Lq > Lk under a causal
+ * mask) get o = 0 and lse = -inf.  Variable-length attention is a title on the
+ * pages (FlashMask, PagedAttention in the FlashAttention-2 (PL) literature);
+ * the packing and the alignment are this library's readings.
+ *
+ *   q, o          [total_q][Hq][d] (token-major), element type dtype (BF16/F16).
+ *   k, v          [total_k][Hkv][d].
+ *   lse           [Hq][total_q] float32 (natural log), or NULL.
+ *   cu_seqlens_q, cu_seqlens_k  device int32 [B+1], nondecreasing, from 0 to
+ *                 total_q / total_k (the kernel clamps them into range, so
+ *                 inconsistent offsets give unspecified values, never an
+ *                 access outside the tensors).
+ *   max_seqlen_q, max_seqlen_k  upper bounds of Lq and Lk over the batch;
+ *                 query rows beyond max_seqlen_q are not computed.
+ *   B, Hq, Hkv, d, causal, window_left, scale, stream  as for fa_fwd.
+ *
+ * Errors as for fa_fwd; FA_DTYPE_F32 is FA_ERR_UNSUPPORTED; max_seqlen_k * Hkv
+ * * d * 2 bytes must stay below 2 GiB.
+ */
+int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                  const int *cu_seqlens_q, const int *cu_seqlens_k, int B, int Hq, int Hkv,
+                  int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
+                  int causal, int window_left, float scale, void *stream, fa_dtype_t dtype);
+
+/*
  * Attention forward on FP8 inputs with per-tensor scales.
  *
  * The FlashAttention quiz (question 6) and the FlashAttention-2 (PL) article

@@ -272,3 +272,43 @@ def test_kvcache_workspace_size():
     # a short cache is never cut below four 32-key tiles per split
     assert _lib.fa_fwd_kvcache_num_splits(1, 8, 8, 1, 100) == 1
     assert _lib.fa_fwd_kvcache_num_splits(1, 8, 8, 1, 32768) >= 8
+
+
+# packed variable-length forward: fake addresses
+CQ, CK = 0xE00000, 0xF00000
+GOOD_VL = dict(q=Q, k=K, v=V, o=O, lse=L, cq=CQ, ck=CK, B=2, Hq=4, Hkv=2, tq=40, tk=50, mq=30, mk=30, d=64,
+               causal=1, window_left=-1, scale=0.125, stream=None)
+
+
+def call_vl(dtype=_lib.FA_DTYPE_BF16, **over):
+    a = dict(GOOD_VL, **over)
+    return _lib.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"], a["B"], a["Hq"],
+                              a["Hkv"], a["tq"], a["tk"], a["mq"], a["mk"], a["d"], a["causal"], a["window_left"],
+                              a["scale"], a["stream"], dtype)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(B=-1), _lib.FA_ERR_INVALID_ARG),
+    (dict(tk=-1), _lib.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), _lib.FA_ERR_INVALID_ARG),
+    (dict(window_left=-2), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), _lib.FA_ERR_UNSUPPORTED),
+    (dict(d=80), _lib.FA_ERR_UNSUPPORTED),
+    (dict(cq=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(ck=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(cq=CQ + 2), _lib.FA_ERR_MISALIGNED),
+    (dict(o=O + 8), _lib.FA_ERR_MISALIGNED),
+    (dict(o=Q), _lib.FA_ERR_INVALID_ARG),
+    (dict(lse=O + 16), _lib.FA_ERR_INVALID_ARG),
+    (dict(mk=2 ** 24), _lib.FA_ERR_UNSUPPORTED),
+])
+def test_varlen_validation_rejects(over, status):
+    assert call_vl(**over) == status
+    assert _lib.fa_last_error() != ""
+
+
+def test_varlen_f32_and_empty():
+    assert call_vl(dtype=_lib.FA_DTYPE_F32) == _lib.FA_ERR_UNSUPPORTED
+    assert call_vl(B=0, q=0, k=0, v=0, o=0, lse=0, cq=0, ck=0) == _lib.FA_OK
+    assert call_vl(tq=0) == _lib.FA_OK
+    assert call_vl(mq=0) == _lib.FA_OK

@@ -320,6 +320,65 @@ def decode_bytes(w: DecodeWorkload, seqlens, elem: int = 2) -> int:
     return (2 * kv * w.Hkv * w.d * elem + w.B * w.Hq * w.Nq * w.d * elem * 2 + w.B * w.Hq * w.Nq * 4)
 
 
+# ---------------------------------------------------------------------------
+# Packed sequences of different lengths (prefill of a mixed batch): B lengths
+# drawn from integers(lo, hi + 1) by a generator seeded with the workload's
+# seed, then Q, K, V standard normal in float32 over the packed shapes
+# [total][H][d] from the same generator, rounded to the storage type.  Query
+# and key counts are equal per sequence (self-attention).
+
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    name: str
+    dtype: str
+    B: int
+    Hq: int
+    Hkv: int
+    lo: int
+    hi: int
+    d: int
+    causal: bool
+    window_left: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    def replace(self, **kw) -> "VarlenWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+VARLEN_WORKLOADS = {
+    # 16 sequences of 512..8192 tokens, causal, MHA d=128 (a mixed training or prefill batch)
+    "varlen_causal_16": VarlenWorkload("varlen_causal_16", "bf16", 16, 16, 16, 512, 8192, 128, True, -1, 8),
+}
+
+
+def make_varlen_inputs(w: VarlenWorkload, **over):
+    """(q, k, v, cu_seqlens) for a packed workload: q [total][Hq][d], k, v
+    [total][Hkv][d] float32 exact in w.dtype, cu_seqlens int32 [B+1]."""
+    w = w.replace(**over) if over else w
+    rng = np.random.default_rng(w.seed)
+    lens = rng.integers(w.lo, w.hi + 1, w.B)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    total = int(cu[-1])
+    q = rng.standard_normal((total, w.Hq, w.d), dtype=np.float32)
+    k = rng.standard_normal((total, w.Hkv, w.d), dtype=np.float32)
+    v = rng.standard_normal((total, w.Hkv, w.d), dtype=np.float32)
+    return round_to(w.dtype, q), round_to(w.dtype, k), round_to(w.dtype, v), cu
+
+
+def varlen_metric_flops(w: VarlenWorkload, cu) -> float:
+    """4*d FLOPs per visible (query, key) pair per head, summed over the
+    sequences (exact visible pairs: L(L+1)/2 per causal sequence)."""
+    total = 0.0
+    for a, b in zip(cu[:-1], cu[1:]):
+        L = int(b - a)
+        total += float(unmasked_pairs(L, w.causal, w.window_left))
+    return 4.0 * w.Hq * w.d * total
+
+
 def unmasked_pairs(N: int, causal: bool, window_left: int) -> int:
     """Number of (query i, key j) pairs that a causal and/or left-window mask
     keeps, per head: key j is kept when j <= i (if causal) and j >= i - wl
