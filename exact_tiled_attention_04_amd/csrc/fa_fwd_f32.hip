@@ -69,19 +69,32 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c = p.scale_log2;
 
+  // The next tile's K and V travel in registers while the current tile is
+  // computed (one global round trip per tile is hidden behind the compute).
+  constexpr int kPer = kTile4 / kThreads;  // float4 of K (and of V) per thread per tile
+  float4 nk[kPer], nv[kPer];
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int idx = tid + u * kThreads;
+      const int key = t * kKeys + idx / kRow4;
+      const int c4 = idx % kRow4;
+      const bool in = t < t_end && key < N;
+      nk[u] = in ? kg[(long long)key * kRow4 + c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+      nv[u] = in ? vg[(long long)key * kRow4 + c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  fetch(t_beg);
   for (int t = t_beg; t < t_end; ++t) {
     const int kb = t * kKeys;
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < kTile4 / kThreads; ++u) {
-      const int idx = tid + u * kThreads;
-      const int key = kb + idx / kRow4;
-      const int c4 = idx % kRow4;
-      const bool in = key < N;
-      sK[idx] = in ? kg[(long long)key * kRow4 + c4] : make_float4(0.f, 0.f, 0.f, 0.f);
-      sV[idx] = in ? vg[(long long)key * kRow4 + c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = 0; u < kPer; ++u) {
+      sK[tid + u * kThreads] = nk[u];
+      sV[tid + u * kThreads] = nv[u];
     }
     __syncthreads();
+    fetch(t + 1);
     // every key of the tile hidden from every row of the workgroup
     if ((causal && kb > qlast) || (wl >= 0 && kb + kKeys - 1 < q0 - wl)) continue;
 
