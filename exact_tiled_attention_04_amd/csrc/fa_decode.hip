@@ -187,11 +187,24 @@ __global__ void __launch_bounds__(kWaves * kWaveSize) decode_split_kernel(Decode
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
-  // Workgroups go to the 8 XCDs round-robin; each XCD takes a contiguous
-  // slice of the logical order (batch * Hkv + head, split, row block), so the
-  // row blocks that stream the same tiles share one L2.
-  const int item = xcd_slice_index(blockIdx.x, gridDim.x) * kWaves + wave;
-  if (item >= p.total_items) return;  // whole wavefronts only; no barrier follows
+  // Workgroups go to the 8 XCDs round-robin (workgroup id mod 8).  A unit
+  // (batch * Hkv + head, split) goes to XCD unit mod 8 with its row blocks
+  // together (they stream the same tiles, shared through that XCD's L2), so
+  // every XCD gets units of every sequence: caches of different lengths do
+  // not leave some XCDs with far more work than others.  The grid holds
+  // 8 * ceil(units / 8) units; the missing ones return at once.
+  int item;
+  if constexpr (kWaves == 1) {
+    const int xcd = blockIdx.x % 8;
+    const int r = blockIdx.x / 8;
+    const int u_local = r / p.n_row_blocks;
+    const int unit = 8 * u_local + xcd;
+    if (unit >= p.total_items / p.n_row_blocks) return;
+    item = unit * p.n_row_blocks + (r - u_local * p.n_row_blocks);
+  } else {
+    item = xcd_slice_index(blockIdx.x, gridDim.x) * kWaves + wave;
+    if (item >= p.total_items) return;  // whole wavefronts only; no barrier follows
+  }
 
   const int rb = item % p.n_row_blocks;
   const int rest = item / p.n_row_blocks;
@@ -438,7 +451,8 @@ __global__ void __launch_bounds__(kMergeRows * kWaveSize) decode_merge_kernel(De
 
 template <typename E, int D>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-  const int blocks = (p.total_items + kWaves - 1) / kWaves;
+  const int units = p.total_items / p.n_row_blocks;
+  const int blocks = kWaves == 1 ? 8 * ((units + 7) / 8) * p.n_row_blocks : (p.total_items + kWaves - 1) / kWaves;
   if (p.block_table)
     hipLaunchKernelGGL((decode_split_kernel<E, D, true>), dim3(blocks), dim3(kWaves * kWaveSize), 0, stream, p);
   else
