@@ -181,6 +181,13 @@ def main():
             gui = statistics.mean(a["GRBM_GUI_ACTIVE"]) / 8
             util = statistics.mean(a["SQ_VALU_MFMA_BUSY_CYCLES"]) / (gui * simd)
             lines.append(f"  MFMA busy cycles / (GPU-active cycles per XCD x 1024 SIMDs) = {100 * util:.1f}%")
+        for mops in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_F8"):
+            if mops in a:
+                # the counter is in units of 512 FLOPs of MFMA work
+                mf = statistics.mean(a[mops]) * 512
+                util = mf / (tr["avg_us"] * 1e-6) / (args.peak * 1e12)
+                lines.append(f"  MFMA FLOPs from {mops} x 512 = {mf:.4e} per launch -> {100 * util:.1f}% of "
+                             f"{args.peak} TFLOP/s over the trace's average duration")
         if "SQ_LDS_BANK_CONFLICT" in a and "SQ_LDS_IDX_ACTIVE" in a:
             bc = statistics.mean(a["SQ_LDS_BANK_CONFLICT"]) / max(1.0, statistics.mean(a["SQ_LDS_IDX_ACTIVE"]))
             lines.append(f"  LDS bank-conflict cycles / LDS active cycles = {100 * bc:.2f}%")
