@@ -3,6 +3,7 @@ bf16/fp16 matrix-core peak.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload causal_8k]
                     [--no-cpu-baseline] [--all] [--copy-calibration MiB] [--bwd] [--fp8] [--decode [--splits S]] [--varlen]
+                    [--matrix-ceiling]
 
 One step = one forward call (the whole path: Q/K/V tile staging, both
 contractions, online softmax, epilogue) over seeded synthetic inputs already
@@ -22,6 +23,12 @@ decoding workload), as algorithmic bytes per second against HBM bandwidth.
 ``--varlen`` times the packed variable-length forward on
 ``varlen_causal_16`` (16 sequences of 512-8192 tokens), FLOPs over the exact
 visible pairs of every sequence.
+
+``--matrix-ceiling`` times the vendor bf16 GEMM (torch.matmul, hipBLASLt) on
+square 8192^3 and 16384^3 products, once with inputs drawn like the headline
+workload's and once with zeros: a reference for how much of the nominal
+matrix-core peak the chip sustains under its power limit with such data
+(library code, not part of the attention path).
 
 ``--bwd`` times the backward instead (one step = one ``fa.bwd`` call: the
 row-term prep, dK/dV and dQ kernels) from the forward's o and lse, credited
@@ -534,6 +541,37 @@ def run_varlen(args, name, with_cpu):
     return rec
 
 
+def run_matrix_ceiling(args):
+    """bf16 GEMM throughput of the vendor library on inputs like the headline
+    workload's (0.5 * N(0, 1), rounded to bf16) and on zeros, one JSON line
+    per case: the matrix cores' sustained rate under the power limit depends
+    on the data's bit activity, which sets the clock."""
+    import torch
+    recs = []
+    for M in (8192, 16384):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(2)
+        a = (torch.randn(M, M, device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+        b = (torch.randn(M, M, device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+        for data in ("0.5*N(0,1)", "zeros"):
+            if data == "zeros":
+                a.zero_()
+                b.zero_()
+            steps = max(5, args.steps // (10 if M == 8192 else 40))
+            warm = max(5, args.warmup // (10 if M == 8192 else 40))
+            sub = argparse.Namespace(steps=steps, warmup=warm)
+            stream = torch.cuda.current_stream()
+            _, per_call = time_steps(lambda: torch.matmul(a, b), sub, f"gemm {M} {data}", stream)
+            ms = sorted(per_call)[len(per_call) // 2]
+            tf = 2.0 * M ** 3 / (ms * 1e-3) / 1e12
+            recs.append({"metric": "bf16 GEMM TFLOP/s (torch.matmul / hipBLASLt), reference ceiling",
+                         "value": round(tf, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+                         "ms_per_step": round(ms, 4), "higher_is_better": True,
+                         "pct_of_peak": round(100 * tf / PEAK_TFLOPS["bf16"], 1), "dtype": "bf16",
+                         "data": data, "config": {"workload": f"gemm_{M}", "M": M, "N": M, "K": M}})
+    return recs
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -555,6 +593,8 @@ def main():
     ap.add_argument("--splits", type=int, default=None, help="--decode: split count (default: the library's)")
     ap.add_argument("--varlen", action="store_true",
                     help="time the packed variable-length forward (workload varlen_causal_16)")
+    ap.add_argument("--matrix-ceiling", action="store_true",
+                    help="time the vendor bf16 GEMM on headline-like data and on zeros (reference)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the forward kernel runs on a single device "
@@ -566,6 +606,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     import workloads as W
+    if args.matrix_ceiling:
+        for rec in run_matrix_ceiling(args):
+            print(json.dumps(rec), flush=True)
+        return
     if args.varlen:
         name = args.workload if args.workload in W.VARLEN_WORKLOADS else "varlen_causal_16"
         print(json.dumps(run_varlen(args, name, not args.no_cpu_baseline)), flush=True)
