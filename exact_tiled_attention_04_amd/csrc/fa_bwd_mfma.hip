@@ -22,10 +22,10 @@
 //   1. prep: D_i and lse_i * log2(e) for every row, into the caller's
 //      workspace;
 //   2. dK/dV: one workgroup per (batch, key/value head, block of 128 keys);
-//      each of its 4 wavefronts owns 32 keys and keeps their K and V rows in
-//      registers as MFMA operands and their dK^T, dV^T in accumulators, while
-//      64-row tiles of Q, dO, lse, D of every query head in the group stream
-//      through LDS;
+//      each group of its wavefronts owns 32 keys, takes their K and V rows as
+//      MFMA operands (from registers at d = 64, from LDS at d = 128) and keeps
+//      their dK^T, dV^T in accumulators, while 64-row tiles of Q, dO, lse, D
+//      of every query head in the group stream through LDS;
 //   3. dQ: one workgroup per (batch, query head, block of 128 queries), the
 //      forward's layout: each wavefront owns 32 queries, 64-key tiles of K and
 //      V stream through LDS.
@@ -159,21 +159,6 @@ __device__ __forceinline__ f32x16 rows_times_own(const unsigned short* __restric
   return acc;
 }
 
-// The same product with the wavefront's own rows read from LDS as B operands
-// (own rows own_row0 .. own_row0+31 of `own`, stored like a streamed tile).
-template <typename E, int D>
-__device__ __forceinline__ f32x16 rows_times_lds(const unsigned short* __restrict__ t, int h, int l32, int hh,
-                                                 const unsigned short* __restrict__ own, int own_row0) {
-  f32x16 acc = f32x16{};
-#pragma unroll
-  for (int kc = 0; kc < Shape<D>::kSteps; ++kc) {
-    const u32x4 a = *(const u32x4*)(t + row_off<D>(32 * h + l32, 2 * kc + hh));
-    const u32x4 b = *(const u32x4*)(own + row_off<D>(own_row0 + l32, 2 * kc + hh));
-    acc = E::mma(a, b, acc);
-  }
-  return acc;
-}
-
 // Load a row of 16-bit elements as the wavefront's B operands (lane holds
 // elements 16kc + 8hh .. +7 for k-step kc); zero past the end.
 template <int D>
@@ -269,11 +254,45 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
 constexpr int kDkvWaves = 8;
 constexpr int kDkvThreads = kWaveSize * kDkvWaves;
 
-// At D = 128 the V rows of the workgroup's keys are read from LDS as MFMA
-// operands instead of living in registers (32 VGPRs a lane): with two
-// wavefronts per SIMD each has 256 registers in all.
+// At D = 128 the K and V rows of the workgroup's keys are read from LDS as
+// MFMA operands instead of living in registers (32 VGPRs a lane each): with
+// two wavefronts per SIMD each has 256 registers in all, and the freed ones
+// let the score products' LDS reads run ahead of the products.
 template <int D>
-constexpr bool kVInLds = D == 128;
+constexpr bool kKvInLds = D == 128;
+
+// k-steps by which the LDS reads of S and dP run ahead of their products
+constexpr int kScoreReadLead = 2;
+
+// S = Q K^T and dP = dO V^T for the wavefront's 32 keys and the 32 query
+// rows 32qh.. of the tile, the keys' K and V rows read from LDS (stored like
+// a streamed tile, rows own_row0..): the two products alternate k-steps, and
+// each k-step's four reads are issued kScoreReadLead k-steps early.
+template <typename E, int D>
+__device__ __forceinline__ void scores_from_lds(const unsigned short* __restrict__ tq,
+                                                const unsigned short* __restrict__ to,
+                                                const unsigned short* __restrict__ kk,
+                                                const unsigned short* __restrict__ vk, int own_row0, int qh,
+                                                int l32, int hh, f32x16& s, f32x16& dp) {
+  constexpr int kS = Shape<D>::kSteps;
+  s = f32x16{};
+  dp = f32x16{};
+#pragma unroll
+  for (int kc = 0; kc < kS; ++kc) {
+    const u32x4 aq = *(const u32x4*)(tq + row_off<D>(32 * qh + l32, 2 * kc + hh));
+    const u32x4 bk = *(const u32x4*)(kk + row_off<D>(own_row0 + l32, 2 * kc + hh));
+    const u32x4 ao = *(const u32x4*)(to + row_off<D>(32 * qh + l32, 2 * kc + hh));
+    const u32x4 bv = *(const u32x4*)(vk + row_off<D>(own_row0 + l32, 2 * kc + hh));
+    s = E::mma(aq, bk, s);
+    dp = E::mma(ao, bv, dp);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 * kScoreReadLead, 0);  // LDS read
+#pragma unroll
+  for (int kc = 0; kc < kS; ++kc) {
+    if (kc + kScoreReadLead < kS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                // MFMA
+  }
+}
 
 template <typename E, int D>
 __global__ void __launch_bounds__(kDkvThreads) bwd_dkdv_kernel(BwdParams p) {
@@ -285,7 +304,8 @@ __global__ void __launch_bounds__(kDkvThreads) bwd_dkdv_kernel(BwdParams p) {
   unsigned short(*sO)[kTile * D] = sT[1];  // dO tiles
   __shared__ __attribute__((aligned(16))) float sL[2][kTile];               // lse * log2(e)
   __shared__ __attribute__((aligned(16))) float sD[2][kTile];               // D
-  __shared__ __attribute__((aligned(16))) unsigned short sVk[kVInLds<D> ? kBlock * D : 8];  // V rows of the block
+  __shared__ __attribute__((aligned(16))) unsigned short sKk[kKvInLds<D> ? kBlock * D : 8];  // K rows of the block
+  __shared__ __attribute__((aligned(16))) unsigned short sVk[kKvInLds<D> ? kBlock * D : 8];  // V rows of the block
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWaveSize - 1);
@@ -308,9 +328,11 @@ __global__ void __launch_bounds__(kDkvThreads) bwd_dkdv_kernel(BwdParams p) {
   const int myk = kw0 + l32;
   const long long kv_head = ((long long)b * p.Hkv + hk) * N * D;
 
-  u32x4 kf[S::kSteps], vf[kVInLds<D> ? 1 : S::kSteps];
-  load_own_row<D>((const unsigned short*)p.k + kv_head + (long long)myk * D, myk < N, hh, kf);
-  if (!kVInLds<D>) load_own_row<D>((const unsigned short*)p.v + kv_head + (long long)myk * D, myk < N, hh, vf);
+  u32x4 kf[kKvInLds<D> ? 1 : S::kSteps], vf[kKvInLds<D> ? 1 : S::kSteps];
+  if (!kKvInLds<D>) {
+    load_own_row<D>((const unsigned short*)p.k + kv_head + (long long)myk * D, myk < N, hh, kf);
+    load_own_row<D>((const unsigned short*)p.v + kv_head + (long long)myk * D, myk < N, hh, vf);
+  }
   f32x16 dk[S::kOutTiles], dv[S::kOutTiles];
 #pragma unroll
   for (int ct = 0; ct < S::kOutTiles; ++ct) dk[ct] = dv[ct] = f32x16{};
@@ -343,11 +365,14 @@ __global__ void __launch_bounds__(kDkvThreads) bwd_dkdv_kernel(BwdParams p) {
     if (wave == 1) copy_vec(head_rsrc(p.delta, 4 * bh * N, 4 * N), sD[buf], q0, lane);
   };
 
-  if (kVInLds<D>) {  // rows k0 .. k0+127 of V (zeros past the end)
+  if (kKvInLds<D>) {  // rows k0 .. k0+127 of K and V (zeros past the end)
 #pragma unroll
-    for (int part = 0; part < kBlock / kTile; ++part)
+    for (int part = 0; part < kBlock / kTile; ++part) {
+      copy_tile<D, kDkvWaves>(head_rsrc(p.k, 2 * kv_head, head_bytes), co, sKk + part * kTile * D,
+                              k0 + part * kTile, wave);
       copy_tile<D, kDkvWaves>(head_rsrc(p.v, 2 * kv_head, head_bytes), co, sVk + part * kTile * D,
                               k0 + part * kTile, wave);
+    }
   }
   issue(0, 0);
   barrier_all();
@@ -362,9 +387,13 @@ __global__ void __launch_bounds__(kDkvThreads) bwd_dkdv_kernel(BwdParams p) {
     if (any) {
       const bool need_mask = qs + 32 > N || kw0 + kRows > N || (p.causal && qs < kw0 + kRows - 1) ||
                              (wl >= 0 && qs + 31 > kw0 + wl);
-      const f32x16 s = rows_times_own<E, D>(sQ[buf], qh, l32, hh, kf);  // S[query][key]
-      const f32x16 dp = kVInLds<D> ? rows_times_lds<E, D>(sO[buf], qh, l32, hh, sVk, kg * kRows)
-                                   : rows_times_own<E, D>(sO[buf], qh, l32, hh, vf);
+      f32x16 s, dp;  // S[query][key], dP[query][key]
+      if constexpr (kKvInLds<D>) {
+        scores_from_lds<E, D>(sQ[buf], sO[buf], sKk, sVk, kg * kRows, qh, l32, hh, s, dp);
+      } else {
+        s = rows_times_own<E, D>(sQ[buf], qh, l32, hh, kf);
+        dp = rows_times_own<E, D>(sO[buf], qh, l32, hh, vf);
+      }
       float pv[16], dsv[16];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
