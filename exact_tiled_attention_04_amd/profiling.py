@@ -21,6 +21,7 @@ files under ``profiles/``.
           against 8000 GB/s)
 --name    output base name (default: fwd_<workload>; the traffic JSON that
           bench.py reads is written only for the forward)
+--note    a paragraph appended to the summary (repeatable)
 """
 from __future__ import annotations
 
@@ -39,6 +40,19 @@ KERNEL_KEY = "fwd_"
 # sources each forward kernel is compiled from (its launch, host code aside)
 FWD_SOURCES = ("fa_fwd_mfma.hip", "fa_mfma_common.h", "fa_internal.h")
 FP8_SOURCES = ("fa_fwd_fp8.hip", "fa_mfma_common.h", "fa_internal.h")
+BWD_SOURCES = ("fa_bwd_mfma.hip", "fa_mfma_common.h", "fa_internal.h")
+DECODE_SOURCES = ("fa_decode.hip", "fa_decode.h", "fa_mfma_common.h", "fa_internal.h")
+
+
+def sources_of(kernel_key: str, fp8: bool = False):
+    """The source files of the kernel a --kernel substring selects."""
+    if fp8 or "fp8" in kernel_key:
+        return FP8_SOURCES
+    if "bwd" in kernel_key:
+        return BWD_SOURCES
+    if "decode" in kernel_key:
+        return DECODE_SOURCES
+    return FWD_SOURCES
 
 
 def kernel_source_hash(sources=FWD_SOURCES) -> str:
@@ -119,11 +133,12 @@ def main():
                     help="algorithmic bytes per launch (HBM-bound kernels), priced against 8000 GB/s")
     ap.add_argument("--fp8", action="store_true", help="the FP8 forward kernel (its sources for the hash)")
     ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
+    ap.add_argument("--note", action="append", default=[], help="a paragraph appended to the summary")
     args = ap.parse_args()
     global KERNEL_KEY
     KERNEL_KEY = args.kernel
     forward = args.kernel in ("fwd_", "fwd_fp8")
-    sources = FP8_SOURCES if args.fp8 else FWD_SOURCES
+    sources = sources_of(args.kernel, args.fp8)
     name = args.name or f"fwd_{args.workload}"
 
     tr = trace_summary(args.trace, args.last)
@@ -191,6 +206,8 @@ def main():
         if "SQ_LDS_BANK_CONFLICT" in a and "SQ_LDS_IDX_ACTIVE" in a:
             bc = statistics.mean(a["SQ_LDS_BANK_CONFLICT"]) / max(1.0, statistics.mean(a["SQ_LDS_IDX_ACTIVE"]))
             lines.append(f"  LDS bank-conflict cycles / LDS active cycles = {100 * bc:.2f}%")
+    for note in args.note:
+        lines += ["", note]
     lines.append(f"\nkernel sources sha256 {kernel_source_hash(sources)}")
     out = os.path.join(args.out_dir, f"{name}.md")
     open(out, "w").write("\n".join(lines) + "\n")
