@@ -93,6 +93,20 @@ def trace_summary(d, last=None):
             "agpr": rows[0].get("Accum_VGPR_Count") if rows else None}
 
 
+def stats_summary(d):
+    """The kernel's row of rocprofv3's --stats table (every dispatch, warm-up
+    included), or None when the run wrote none."""
+    try:
+        rows = _csv(d, "kernel_stats.csv")
+    except FileNotFoundError:
+        return None
+    for r in rows:
+        if _is_attn(r["Name"]):
+            return {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                    "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3}
+    return None
+
+
 def counter_per_dispatch(d, last=None):
     """{counter: [value per dispatch]} for the attention kernel, plus the copy kernel."""
     rows = _csv(d, "counter_collection.csv")
@@ -151,6 +165,10 @@ def main():
               f"trace fields VGPR_Count {tr['vgpr']}, Accum_VGPR_Count {tr['agpr']} (the compiler's resource report is the authority on register use)", "",
               f"kernel trace, last {tr['dispatches']} dispatches: avg {tr['avg_us']:.1f} us, "
               f"min {tr['min_us']:.1f} us, max {tr['max_us']:.1f} us"]
+    st = stats_summary(args.trace)
+    if st:
+        lines.append(f"rocprofv3 --stats, all {st['calls']} dispatches (warm-up included): avg {st['avg_us']:.1f} us, "
+                     f"min {st['min_us']:.1f} us, max {st['max_us']:.1f} us")
     if args.flops:
         lines.append(f"algorithmic FLOPs per launch {args.flops:.4e} -> {args.flops / (tr['avg_us'] * 1e-6) / 1e12:.1f} "
                      f"TFLOP/s at the average duration ({100 * args.flops / (tr['avg_us'] * 1e-6) / (args.peak * 1e12):.1f}% "
