@@ -292,15 +292,17 @@ __device__ __forceinline__ float tile_softmax(const LoopCtx<D>& x, RowState<D>& 
 
 // O^T += V^T P^T for one tile.  k-step mc covers keys 16mc..16mc+15 in the
 // order the score accumulator hands them over: half-wave hh holds keys
-// 16mc + 4hh + {0..3} and 16mc + 8 + 4hh + {0..3}.
+// 16mc + 4hh + {0..3} and 16mc + 8 + 4hh + {0..3}.  The k-steps are the outer
+// loop, so consecutive products share their P^T operand (measured ~0.7%
+// faster than output tile by output tile, bit-identical).
 template <typename E, int D>
 __device__ __forceinline__ void tile_pv(const unsigned short* __restrict__ vC, const LoopCtx<D>& x,
                                         RowState<D>& st, const u32x4* pf) {
 #pragma unroll
-  for (int ct = 0; ct < Shape<D>::kOutTiles; ++ct) {
-    const int col = 32 * ct + x.v_col_lane;
+  for (int mc = 0; mc < 2 * kHalves; ++mc) {
 #pragma unroll
-    for (int mc = 0; mc < 2 * kHalves; ++mc) {
+    for (int ct = 0; ct < Shape<D>::kOutTiles; ++ct) {
+      const int col = 32 * ct + x.v_col_lane;
       const int ra = 16 * mc + x.v_row_lane;
       const s16x4 lo = lds_read_tr(vC, v_off<D>(ra, col));
       const s16x4 hi = lds_read_tr(vC, v_off<D>(ra + 8, col));
