@@ -10,7 +10,9 @@ of ``include/fa.h``).  This package is a thin binding:
                 ``fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, ...)``,
                 ``fwd_kvcache(q, k_cache, v_cache, cache_seqlens, ...)``,
                 ``fwd_kvcache_paged(q, k_pages, v_pages, block_table, ...)`` and
-                ``bwd(q, k, v, o, lse, dout, ...)`` on torch tensors
+                ``bwd(q, k, v, o, lse, dout, ...)`` on torch tensors, and
+                ``attend(q, k, v, ...)``, the forward as a differentiable
+                torch operation whose backward is ``bwd``
     build       compiles libfa.so in-tree with hipcc
 """
 from ._lib import FaError, LIB_PATH, load  # noqa: F401
@@ -46,4 +48,10 @@ def bwd(*args, **kwargs):
     return _bwd(*args, **kwargs)
 
 
-__all__ = ["fwd", "fwd_varlen", "fwd_fp8", "fwd_kvcache", "fwd_kvcache_paged", "bwd", "FaError", "LIB_PATH", "load"]
+def attend(*args, **kwargs):
+    from .attention import attend as _a
+    return _a(*args, **kwargs)
+
+
+__all__ = ["fwd", "fwd_varlen", "fwd_fp8", "fwd_kvcache", "fwd_kvcache_paged", "bwd", "attend", "FaError",
+           "LIB_PATH", "load"]

@@ -310,3 +310,33 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
     if status != _lib.FA_OK:
         raise _lib.FaError(status, _lib.fa_last_error())
     return dq, dk, dv
+
+
+class _Attention(torch.autograd.Function):
+    """``fwd`` as a differentiable torch operation: the forward saves q, k, v,
+    o and lse, the backward calls ``bwd`` with them."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal, window_left, scale):
+        o, lse = fwd(q, k, v, causal=causal, window_left=window_left, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.args = (causal, window_left, scale)
+        ctx.mark_non_differentiable(lse)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, dout, _dlse):
+        q, k, v, o, lse = ctx.saved_tensors
+        causal, window_left, scale = ctx.args
+        dq, dk, dv = bwd(q, k, v, o, lse, dout.contiguous(), causal=causal, window_left=window_left, scale=scale)
+        return dq, dk, dv, None, None, None
+
+
+def attend(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, window_left: int = -1,
+           scale: Optional[float] = None) -> torch.Tensor:
+    """Differentiable exact attention: returns o like ``fwd`` and, when a loss
+    built on it is backpropagated, the gradients of q, k and v from ``bwd``
+    (float16/bfloat16; the logsumexp the backward needs is kept internally).
+    """
+    o, _ = _Attention.apply(q, k, v, causal, window_left, scale)
+    return o

@@ -209,3 +209,22 @@ def test_bwd_side_stream_and_caller_buffers():
     s.synchronize()
     for x, y in zip((dq, dk, dv), ref):
         np.testing.assert_array_equal(x.double().cpu().numpy(), y)
+
+
+def test_differentiable_attention_matches_fwd_and_bwd():
+    """fa.attend under torch autograd gives the same bits as calling fwd
+    and bwd directly, and its gradients are within the oracle's bound."""
+    q, k, v = random_inputs(995, "bf16", 1, 4, 2, 200, 128)
+    do = random_grad(996, "bf16", 1, 4, 200, 128)
+    ref = run_bwd_gpu(q, k, v, do, "bf16", True, 60, 0.1, "autograd reference")
+    qd, kd, vd, dod = (to_dev(x, "bf16").requires_grad_(i < 3) for i, x in enumerate((q, k, v, do)))
+    announce("autograd attention")
+    o = fa.attend(qd, kd, vd, causal=True, window_left=60, scale=0.1)
+    o_direct, _ = fa.fwd(qd.detach(), kd.detach(), vd.detach(), causal=True, window_left=60, scale=0.1)
+    (o * dod).sum().backward()
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o_direct)
+    for t, r in zip((qd, kd, vd), ref):
+        np.testing.assert_array_equal(t.grad.double().cpu().numpy(), r)
+    grads, mag = oracle_grads(q, k, v, do, True, 60, 0.1)
+    check_grads(ref, grads, mag, "bf16", 200, "autograd")
