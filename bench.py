@@ -408,7 +408,9 @@ def run_decode(args, name, with_cpu):
     else:
         kd, vd = (torch.from_numpy(x).to(tdt).cuda() for x in (k, v))
         nk = w.Nk
-    splits = args.splits if args.splits else fa._lib.fa_fwd_kvcache_num_splits(w.B, w.Hq, w.Hkv, w.Nq, nk)
+    # the caller knows its cache lengths: let the library pick splits for them
+    splits = args.splits if args.splits else fa.kvcache_num_splits(lens, w.Hq, w.Hkv, w.Nq, nk, w.causal,
+                                                                   w.window_left)
     ws_bytes = fa._lib.fa_fwd_kvcache_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, nk, w.d, splits)
     ws = torch.empty(max(1, ws_bytes // 4), dtype=torch.float32, device="cuda")
 

@@ -43,6 +43,11 @@ def fwd_kvcache_paged(*args, **kwargs):
     return _f(*args, **kwargs)
 
 
+def kvcache_num_splits(*args, **kwargs):
+    from .attention import kvcache_num_splits as _f
+    return _f(*args, **kwargs)
+
+
 def bwd(*args, **kwargs):
     from .attention import bwd as _bwd
     return _bwd(*args, **kwargs)
@@ -53,5 +58,5 @@ def attend(*args, **kwargs):
     return _a(*args, **kwargs)
 
 
-__all__ = ["fwd", "fwd_varlen", "fwd_fp8", "fwd_kvcache", "fwd_kvcache_paged", "bwd", "attend", "FaError",
+__all__ = ["fwd", "fwd_varlen", "fwd_fp8", "fwd_kvcache", "fwd_kvcache_paged", "kvcache_num_splits", "bwd", "attend", "FaError",
            "LIB_PATH", "load"]

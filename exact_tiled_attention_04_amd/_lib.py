@@ -23,7 +23,8 @@ FA_ERR_MISALIGNED = -3
 FA_ERR_HIP = -4
 
 EXPORTED = ["fa_fwd", "fa_fwd_bf16", "fa_fwd_f16", "fa_fwd_f32", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_kvcache",
-            "fa_fwd_kvcache_paged", "fa_fwd_kvcache_num_splits", "fa_fwd_kvcache_workspace_size", "fa_bwd",
+            "fa_fwd_kvcache_paged", "fa_fwd_kvcache_num_splits", "fa_fwd_kvcache_num_splits_for_lengths",
+            "fa_fwd_kvcache_workspace_size", "fa_bwd",
             "fa_bwd_bf16", "fa_bwd_f16", "fa_bwd_workspace_size", "fa_status_string", "fa_last_error", "fa_version"]
 
 _lock = threading.Lock()
@@ -66,6 +67,8 @@ def load() -> ctypes.CDLL:
         lib.fa_fwd_kvcache_paged.restype = I
         lib.fa_fwd_kvcache_num_splits.argtypes = [I, I, I, I, I]
         lib.fa_fwd_kvcache_num_splits.restype = I
+        lib.fa_fwd_kvcache_num_splits_for_lengths.argtypes = [I, I, I, I, I, I, I, P]
+        lib.fa_fwd_kvcache_num_splits_for_lengths.restype = I
         lib.fa_fwd_kvcache_workspace_size.argtypes = [I, I, I, I, I, I, I]
         lib.fa_fwd_kvcache_workspace_size.restype = ctypes.c_size_t
         bwd_args = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
@@ -142,6 +145,11 @@ def fa_fwd_kvcache_paged(q, k_pages, v_pages, block_table, cache_seqlens, o, lse
 
 def fa_fwd_kvcache_num_splits(B: int, Hq: int, Hkv: int, Nq: int, Nk: int) -> int:
     return load().fa_fwd_kvcache_num_splits(B, Hq, Hkv, Nq, Nk)
+
+
+def fa_fwd_kvcache_num_splits_for_lengths(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, causal: int,
+                                          window_left: int, seqlens_host_addr: int) -> int:
+    return load().fa_fwd_kvcache_num_splits_for_lengths(B, Hq, Hkv, Nq, Nk, causal, window_left, seqlens_host_addr)
 
 
 def fa_fwd_kvcache_workspace_size(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, num_splits: int) -> int:

@@ -178,6 +178,18 @@ def _kv_common(q, k, v, out, lse, want_lse, workspace, B, Hq, Hkv, Nq, Nk, d, nu
     return o, lse, workspace, s
 
 
+def kvcache_num_splits(cache_seqlens, Hq: int, Hkv: int, Nq: int, Nk: int, causal: bool = False,
+                       window_left: int = -1) -> int:
+    """The split count ``fa_fwd_kvcache_num_splits_for_lengths`` picks for
+    caches of these lengths (a host sequence or CPU tensor of B ints; Nk is
+    the capacity, page_size * pages per sequence for a paged cache)."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(cache_seqlens.cpu() if isinstance(cache_seqlens, torch.Tensor)
+                                           else cache_seqlens, dtype=np.int32).reshape(-1))
+    return _lib.fa_fwd_kvcache_num_splits_for_lengths(len(lens), Hq, Hkv, Nq, Nk, int(causal), window_left,
+                                                      lens.ctypes.data)
+
+
 def _int32_dev(x, device, name):
     if x is None:
         return None

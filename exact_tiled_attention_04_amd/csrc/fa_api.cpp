@@ -4,6 +4,7 @@
 #include "fa.h"
 
 #include <algorithm>
+#include <vector>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -244,12 +245,17 @@ int run_fp8(const void* q, const void* k, const void* v, float q_scale, float k_
 // caller leaves the choice to the library: about four wavefronts per compute
 // unit (one round of the grid; more splits only add merge work and shorter
 // streams), at least four 32-key tiles per split, at most 128 splits.
-int auto_splits(long long base_items, int Nk) {
+int device_cus() {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
   }
+  return cus;
+}
+
+int auto_splits(long long base_items, int Nk) {
+  const int cus = device_cus();
   const long long target = 4LL * cus;
   long long s = base_items > 0 ? (target + base_items - 1) / base_items : 1;
   const long long max_s = std::max(1LL, ((long long)Nk + 32 * 4 - 1) / (32 * 4));
@@ -494,6 +500,50 @@ int fa_fwd_kvcache_paged(const void* q, const void* k_pages, const void* v_pages
 int fa_fwd_kvcache_num_splits(int B, int Hq, int Hkv, int Nq, int Nk) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || Hq % Hkv != 0) return 1;
   return resolve_splits(B, Hq, Hkv, Nq, Nk, 0);
+}
+
+int fa_fwd_kvcache_num_splits_for_lengths(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int window_left,
+                                          const int* cache_seqlens) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || Hq % Hkv != 0 || window_left < -1 || !cache_seqlens)
+    return 1;
+  (void)causal;  // the rows' union reaches the last cached key either way
+  const int wl = window_left >= Nk ? -1 : window_left;
+  // the chunk a split covers is fixed from the capacity (as the launch fixes it)
+  long long need = ((long long)Nk + 31) / 32;
+  if (wl >= 0) need = std::min(need, ((long long)wl + Nq + 31) / 32 + 1);
+  // tiles each sequence's rows need together: keys up to its last one, from
+  // the window's left edge for its first row
+  std::vector<long long> tiles(B);
+  for (int b = 0; b < B; ++b) {
+    const long long L = std::min<long long>(std::max(cache_seqlens[b], 0), Nk);
+    if (L == 0) {
+      tiles[b] = 0;
+      continue;
+    }
+    const long long lo = wl >= 0 ? std::max(0LL, L - Nq - wl) : 0;
+    tiles[b] = (L - 1) / 32 + 1 - lo / 32;
+  }
+  if (*std::max_element(tiles.begin(), tiles.end()) == 0) return 1;  // nothing to read
+  const long long rb = ((long long)(Hq / Hkv) * Nq + 31) / 32;
+  const long long cus = device_cus();
+  // Measured on MI355X: about three streaming wavefronts per CU keep HBM
+  // busy, and more than four work items per CU (one-wave workgroups whose
+  // LDS stages let four or five share a CU) run in a second round.  Take the
+  // fewest splits that give three streams per CU with at most four items per
+  // CU; when no count does both, the most splits within four items per CU.
+  const long long max_s = std::min(128LL, std::max(1LL, ((long long)Nk + 32 * 4 - 1) / (32 * 4)));
+  long long best_fit = 1;
+  for (long long S = 1; S <= max_s; ++S) {
+    const long long per = std::max(1LL, (need + S - 1) / S);
+    long long chunks = 0;
+    for (int b = 0; b < B; ++b) chunks += (tiles[b] + per - 1) / per;
+    const long long streams = chunks * Hkv, items = streams * rb;
+    if (items <= 4 * cus) {
+      best_fit = S;
+      if (streams >= 3 * cus) return (int)S;
+    }
+  }
+  return (int)best_fit;
 }
 
 size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits) {

@@ -256,6 +256,20 @@ int fa_fwd_kvcache_paged(const void *q, const void *k_pages, const void *v_pages
  * that compute nothing. */
 int fa_fwd_kvcache_num_splits(int B, int Hq, int Hkv, int Nq, int Nk);
 
+/* A split count for caches whose lengths the caller knows on the host
+ * (cache_seqlens_host: B lengths, read here only; pass the result as
+ * num_splits together with the same lengths on the device).  Since a split
+ * covers a fixed share of the capacity, short sequences leave their last
+ * splits empty; this counts the splits that will read keys and takes the
+ * fewest that give about three streaming wavefronts per compute unit while
+ * keeping every work item in one wave of the grid (at most four per unit),
+ * else the most splits within that wave, at least four 32-key tiles per
+ * split and at most 128.  Equal full lengths give fewer splits than
+ * fa_fwd_kvcache_num_splits when three streams per unit already suffice.
+ * Returns 1 for sizes that compute nothing or a null pointer. */
+int fa_fwd_kvcache_num_splits_for_lengths(int B, int Hq, int Hkv, int Nq, int Nk, int causal,
+                                          int window_left, const int *cache_seqlens_host);
+
 /* Workspace bytes fa_fwd_kvcache(_paged) needs for these sizes and
  * num_splits (0 = the library's choice): splits * B * Hq * Nq * (d + 1) *
  * sizeof(float) when more than one split runs, else 0. */

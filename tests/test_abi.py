@@ -274,6 +274,55 @@ def test_kvcache_workspace_size():
     assert _lib.fa_fwd_kvcache_num_splits(1, 8, 8, 1, 32768) >= 8
 
 
+def _splits_for(lens, Hq, Hkv, Nq, Nk, causal=1, wl=-1):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(lens, dtype=np.int32))
+    return _lib.fa_fwd_kvcache_num_splits_for_lengths(len(a), Hq, Hkv, Nq, Nk, causal, wl, a.ctypes.data)
+
+
+def _active(lens, Hkv, Nq, Nk, S, wl=-1):
+    """Splits that read keys, as the launch cuts them (each split a fixed
+    share of the capacity), and the work items they make."""
+    need = (Nk + 31) // 32
+    if wl >= 0:
+        need = min(need, (wl + Nq + 31) // 32 + 1)
+    per = max(1, -(-need // S))
+    chunks = 0
+    for L in lens:
+        L = min(max(L, 0), Nk)
+        if L:
+            lo = max(0, L - Nq - wl) if wl >= 0 else 0
+            chunks += -(-((L - 1) // 32 + 1 - lo // 32) // per)
+    return chunks * Hkv
+
+
+def test_kvcache_splits_for_lengths():
+    # no device here: the library assumes 256 compute units
+    rows = lambda Hq, Hkv, Nq: -(-(Hq // Hkv) * Nq // 32)
+    # equal full caches: three streaming wavefronts per unit are enough
+    assert _splits_for([32768] * 8, 32, 8, 1, 32768) == 12
+    # 16 query rows per sequence make two row blocks: four work items per
+    # unit cap the splits before three streams per unit are reached
+    assert _splits_for([16384] * 4, 32, 8, 16, 16384) == 16
+    # caches of varied lengths leave splits empty: more splits than for full ones
+    import numpy as np
+    lens = np.random.default_rng(6).integers(1, 16385, 16)
+    s = _splits_for(lens, 32, 8, 1, 16384)
+    assert s > _splits_for([16384] * 16, 32, 8, 1, 16384)
+    # the choice is the fewest splits meeting the rule, within the limits
+    assert _active(lens, 8, 1, 16384, s) >= 3 * 256 and _active(lens, 8, 1, 16384, s) <= 4 * 256
+    assert _active(lens, 8, 1, 16384, s - 1) < 3 * 256
+    # nothing to read, or no lengths: one split
+    assert _splits_for([0, 0, 0], 32, 8, 1, 16384) == 1
+    assert _lib.fa_fwd_kvcache_num_splits_for_lengths(3, 32, 8, 1, 16384, 1, -1, None) == 1
+    assert _lib.fa_fwd_kvcache_num_splits_for_lengths(3, 30, 8, 1, 16384, 1, -1, None) == 1
+    # short caches keep at least four tiles per split; never above 128
+    assert _splits_for([100], 8, 8, 1, 100) == 1
+    assert 1 <= _splits_for([1 << 20] * 1, 8, 1, 1, 1 << 20) <= 128
+    # a window bounds the keys a split can cover
+    assert _splits_for([32768] * 8, 32, 8, 1, 32768, wl=1000) >= 1
+
+
 # packed variable-length forward: fake addresses
 CQ, CK = 0xE00000, 0xF00000
 GOOD_VL = dict(q=Q, k=K, v=V, o=O, lse=L, cq=CQ, ck=CK, B=2, Hq=4, Hkv=2, tq=40, tk=50, mq=30, mk=30, d=64,

@@ -157,9 +157,11 @@ def test_kvcache_paged_bad_page_index_reads_zeros():
 def test_decode_workload_full_size(name):
     w = DECODE_WORKLOADS[name]
     q, k, v, lens = make_decode_inputs(w)
+    # the split count the benchmark launches with: chosen from the lengths
+    splits = fa.kvcache_num_splits(lens, w.Hq, w.Hkv, w.Nq, w.Nk, w.causal, w.window_left)
     if w.page_size:
-        o, lse = run_paged(q, k, v, lens, w.page_size, w.seed, w.causal, w.window_left, w.scale, w.dtype, 0,
-                           f"{name} full")
+        o, lse = run_paged(q, k, v, lens, w.page_size, w.seed, w.causal, w.window_left, w.scale, w.dtype,
+                           splits, f"{name} full")
     else:
-        o, lse = run_contig(q, k, v, lens, w.causal, w.window_left, w.scale, w.dtype, 0, f"{name} full")
+        o, lse = run_contig(q, k, v, lens, w.causal, w.window_left, w.scale, w.dtype, splits, f"{name} full")
     check(o, lse, q, k, v, lens, w.causal, w.window_left, w.scale, w.dtype, f"{name} full, every row")
