@@ -263,10 +263,17 @@ int auto_splits(long long base_items, int Nk) {
   return (int)std::max(1LL, s);
 }
 
+// Wavefronts per (batch, key/value head, split): the group's G * Nq rows in
+// 32-row blocks, one or two blocks per wavefront.
+long long row_items(int Hq, int Hkv, int Nq) {
+  const long long rb = ((long long)(Hq / Hkv) * Nq + 31) / 32;
+  const int per = fa::decode_row_blocks_per_item((int)std::min<long long>(rb, INT32_MAX));
+  return (rb + per - 1) / per;
+}
+
 int resolve_splits(int B, int Hq, int Hkv, int Nq, int Nk, int num_splits) {
   if (num_splits > 0) return num_splits;
-  const long long rb = ((long long)(Hq / Hkv) * Nq + 31) / 32;
-  return auto_splits((long long)B * Hkv * rb, Nk);
+  return auto_splits((long long)B * Hkv * row_items(Hq, Hkv, Nq), Nk);
 }
 
 uint64_t kvcache_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits) {
@@ -330,8 +337,11 @@ int run_kvcache(const void* q, const void* k, const void* v, const int* block_ta
                      overlap(workspace, n_w, v, n_kv)))
     return fail(FA_ERR_INVALID_ARG, "the workspace overlaps another buffer");
   const long long rb = ((long long)(Hq / Hkv) * Nq + 31) / 32;
-  const long long items = (long long)B * Hkv * rb * splits;
-  if (items > INT32_MAX / 2) return fail(FA_ERR_UNSUPPORTED, "B*Hkv*row blocks*splits=%lld is too many", items);
+  if (rb > INT32_MAX / 2) return fail(FA_ERR_UNSUPPORTED, "Hq/Hkv*Nq=%lld query rows per group is too many", 32 * rb);
+  const int rb_item = fa::decode_row_blocks_per_item((int)rb);
+  const long long row_items = (rb + rb_item - 1) / rb_item;
+  const long long items = (long long)B * Hkv * row_items * splits;
+  if (items > INT32_MAX / 2) return fail(FA_ERR_UNSUPPORTED, "B*Hkv*row items*splits=%lld is too many", items);
 
   fa::DecodeParams p;
   p.q = q;
@@ -366,6 +376,8 @@ int run_kvcache(const void* q, const void* k, const void* v, const int* block_ta
     p.tiles_per_split = (int)std::max(1LL, (need + splits - 1) / splits);
   }
   p.n_row_blocks = (int)rb;
+  p.rb_per_item = rb_item;
+  p.n_row_items = (int)row_items;
   p.total_items = (int)items;
   p.page_size = paged ? page_size : 0;
   p.max_pages = paged ? max_pages : 0;
@@ -524,23 +536,31 @@ int fa_fwd_kvcache_num_splits_for_lengths(int B, int Hq, int Hkv, int Nq, int Nk
     tiles[b] = (L - 1) / 32 + 1 - lo / 32;
   }
   if (*std::max_element(tiles.begin(), tiles.end()) == 0) return 1;  // nothing to read
-  const long long rb = ((long long)(Hq / Hkv) * Nq + 31) / 32;
+  const long long rb = row_items(Hq, Hkv, Nq);
   const long long cus = device_cus();
   // Measured on MI355X: about three streaming wavefronts per CU keep HBM
-  // busy, and more than four work items per CU (one-wave workgroups whose
-  // LDS stages let four or five share a CU) run in a second round.  Take the
-  // fewest splits that give three streams per CU with at most four items per
-  // CU; when no count does both, the most splits within four items per CU.
+  // busy when each owns one 32-row block, four when each owns two (twice the
+  // matrix work per tile), and more than four work items per CU (one-wave
+  // workgroups whose LDS stages let four or five share a CU) run in a second
+  // round.  Take the fewest splits that give that many streams per CU with
+  // at most four items per CU; when no count does both, the most splits
+  // within four items per CU.
+  const long long two = fa::decode_row_blocks_per_item((int)std::min<long long>(
+                            ((long long)(Hq / Hkv) * Nq + 31) / 32, INT32_MAX)) == 2;
+  const long long want = (two ? 4 : 3) * cus;
   const long long max_s = std::min(128LL, std::max(1LL, ((long long)Nk + 32 * 4 - 1) / (32 * 4)));
-  long long best_fit = 1;
+  long long best_fit = 1, best_items = 0;
   for (long long S = 1; S <= max_s; ++S) {
     const long long per = std::max(1LL, (need + S - 1) / S);
     long long chunks = 0;
     for (int b = 0; b < B; ++b) chunks += (tiles[b] + per - 1) / per;
     const long long streams = chunks * Hkv, items = streams * rb;
     if (items <= 4 * cus) {
-      best_fit = S;
-      if (streams >= 3 * cus) return (int)S;
+      if (streams >= want) return (int)S;
+      if (items > best_items) {  // more splits that cut no more chunks only add merge work
+        best_fit = S;
+        best_items = items;
+      }
     }
   }
   return (int)best_fit;

@@ -29,12 +29,17 @@ struct DecodeParams {
   int n_splits;             // splits of each key range (1: o and lse written directly)
   int tiles_per_split;      // 32-key tiles per split, from the capacity (or window) and n_splits
   int n_row_blocks;         // ceil(group * Nq / 32)
-  int total_items;          // B * Hkv * n_row_blocks * n_splits (one wavefront each)
+  int rb_per_item;          // 32-row blocks one wavefront owns (decode_row_blocks_per_item)
+  int n_row_items;          // ceil(n_row_blocks / rb_per_item)
+  int total_items;          // B * Hkv * n_row_items * n_splits (one wavefront each)
   int page_size, max_pages, num_pages;
   float scale_log2;
 };
 
 hipError_t launch_decode(const DecodeParams& p, int d, bool f16, hipStream_t stream);
+// How many 32-row blocks of a GQA group one wavefront takes (1 or 2): two
+// blocks share every K and V tile read into LDS.
+int decode_row_blocks_per_item(int n_row_blocks);
 int decode_waves_per_workgroup();
 
 }  // namespace fa

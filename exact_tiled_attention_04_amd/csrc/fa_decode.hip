@@ -10,10 +10,12 @@
 // Decoding reads the whole cache for very little arithmetic, so the design
 // goal is HBM bandwidth, not matrix-core rate:
 //
-//   * one work item = one wavefront = (batch, key/value head, block of 32
-//     query rows, split of the key range).  The rows of a work item are all
-//     G * Nq query rows of the GQA group that shares the key/value head, so
-//     each cached key is read once per group, not once per query head;
+//   * one work item = one wavefront = (batch, key/value head, one or two
+//     blocks of 32 query rows, split of the key range).  The rows of a work
+//     item are all G * Nq query rows of the GQA group that shares the
+//     key/value head, so each cached key is read once per group, not once
+//     per query head; a group of more than 32 rows gives a wavefront two
+//     blocks, whose products share each K and V read from LDS;
 //   * the visible key range of a (batch, head) is cut into equal splits so
 //     that the grid holds enough wavefronts to keep HBM busy even for one
 //     sequence; each split writes its normalised partial output and its
@@ -58,6 +60,13 @@ constexpr int kTile = 32;  // keys per tile
 #endif
 constexpr int kWaves = FA_DEC_WAVES;    // independent wavefronts per workgroup
 constexpr int kStages = FA_DEC_STAGES;  // K/V tiles in LDS per wavefront
+// A GQA group of more than 32 query rows (G * Nq > 32) gives each wavefront
+// two 32-row blocks, so that every K and V tile it copies into LDS and reads
+// from there serves 64 rows.
+#ifndef FA_DEC_MAX_RB
+#define FA_DEC_MAX_RB 2
+#endif
+constexpr int kMaxRowBlocks = FA_DEC_MAX_RB;
 static_assert(kStages >= 2 && kStages <= 4, "stages");
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kRescaleSlack = 8.0f;   // as in the forward: probabilities stay <= 2^8
@@ -179,7 +188,7 @@ struct Decode {
   }
 };
 
-template <typename E, int D, bool kPaged>
+template <typename E, int D, bool kPaged, int kRB>
 __global__ void __launch_bounds__(kWaves * kWaveSize) decode_split_kernel(DecodeParams p) {
   using S = DShape<D>;
   using K = Decode<E, D, kPaged>;
@@ -188,7 +197,7 @@ __global__ void __launch_bounds__(kWaves * kWaveSize) decode_split_kernel(Decode
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWaveSize);
   // Workgroups go to the 8 XCDs round-robin (workgroup id mod 8).  A unit
-  // (batch * Hkv + head, split) goes to XCD unit mod 8 with its row blocks
+  // (batch * Hkv + head, split) goes to XCD unit mod 8 with its row items
   // together (they stream the same tiles, shared through that XCD's L2), so
   // every XCD gets units of every sequence: caches of different lengths do
   // not leave some XCDs with far more work than others.  The grid holds
@@ -197,17 +206,17 @@ __global__ void __launch_bounds__(kWaves * kWaveSize) decode_split_kernel(Decode
   if constexpr (kWaves == 1) {
     const int xcd = blockIdx.x % 8;
     const int r = blockIdx.x / 8;
-    const int u_local = r / p.n_row_blocks;
+    const int u_local = r / p.n_row_items;
     const int unit = 8 * u_local + xcd;
-    if (unit >= p.total_items / p.n_row_blocks) return;
-    item = unit * p.n_row_blocks + (r - u_local * p.n_row_blocks);
+    if (unit >= p.total_items / p.n_row_items) return;
+    item = unit * p.n_row_items + (r - u_local * p.n_row_items);
   } else {
     item = xcd_slice_index(blockIdx.x, gridDim.x) * kWaves + wave;
     if (item >= p.total_items) return;  // whole wavefronts only; no barrier follows
   }
 
-  const int rb = item % p.n_row_blocks;
-  const int rest = item / p.n_row_blocks;
+  const int ri = item % p.n_row_items;
+  const int rest = item / p.n_row_items;
   const int s = rest % p.n_splits;
   const int bk = rest / p.n_splits;
   const int b = bk / p.Hkv;
@@ -215,23 +224,37 @@ __global__ void __launch_bounds__(kWaves * kWaveSize) decode_split_kernel(Decode
   const int L = min(max(p.seqlens ? scalar_load(p.seqlens, b) : p.Nk, 0), p.Nk);
 
   const int l32 = lane & 31, hh = lane >> 5;
-  const int r = rb * 32 + l32;  // row within the group's G * Nq rows
-  const bool valid = r < p.group * p.Nq;
-  const int g = valid ? r / p.Nq : 0;
-  const int i = valid ? r - g * p.Nq : 0;
-  const int hq = hk * p.group + g;
-  const int pos = L - p.Nq + i;
-  const int lo = p.window_left >= 0 ? max(0, pos - p.window_left) : 0;
-  const int hi = p.causal ? min(pos, L - 1) : L - 1;
-  const bool any = valid && hi >= lo;
-  const long long out_row = ((long long)b * p.Hq + hq) * p.Nq + i;
+  // the wavefront's kRB blocks of 32 rows (rows of the group's G * Nq);
+  // lane l32 holds row l32 of each
+  bool valid[kRB], any[kRB];
+  int lo[kRB];
+  unsigned span[kRB];
+  long long out_row[kRB];
+  int wlo = INT_MAX, whi = -1;
+#pragma unroll
+  for (int j = 0; j < kRB; ++j) {
+    const int r = (ri * kRB + j) * 32 + l32;
+    valid[j] = r < p.group * p.Nq;
+    const int g = valid[j] ? r / p.Nq : 0;
+    const int i = valid[j] ? r - g * p.Nq : 0;
+    const int pos = L - p.Nq + i;
+    lo[j] = p.window_left >= 0 ? max(0, pos - p.window_left) : 0;
+    const int hi = p.causal ? min(pos, L - 1) : L - 1;
+    any[j] = valid[j] && hi >= lo[j];
+    span[j] = (unsigned)(hi - lo[j]);
+    out_row[j] = ((long long)b * p.Hq + hk * p.group + g) * p.Nq + i;
+    if (any[j]) {
+      wlo = min(wlo, lo[j]);
+      whi = max(whi, hi);
+    }
+  }
 
   // this split's tiles: the s-th chunk of tiles_per_split tiles of the range
   // the wavefront's rows need (a chunk size fixed on the host from the
   // cache capacity, so short sequences leave their last splits empty and no
   // split of a long one is longer than any other)
-  const int wlo = wave_min(any ? lo : INT_MAX);
-  const int whi = wave_max(any ? hi : -1);
+  wlo = wave_min(wlo);
+  whi = wave_max(whi);
   int t_beg = 0, t_end = 0;
   if (whi >= wlo) {
     const int tb0 = wlo / kTile, tb1 = whi / kTile + 1;
@@ -240,18 +263,28 @@ __global__ void __launch_bounds__(kWaves * kWaveSize) decode_split_kernel(Decode
     t_end = min(tb1, t_beg + per);
   }
 
-  f32x16 oacc[S::kOutTiles];
+  f32x16 oacc[kRB][S::kOutTiles];
 #pragma unroll
-  for (int ct = 0; ct < S::kOutTiles; ++ct) oacc[ct] = f32x16{};
-  float m_use = -INFINITY, l_run = 0.f;
+  for (int j = 0; j < kRB; ++j)
+#pragma unroll
+    for (int ct = 0; ct < S::kOutTiles; ++ct) oacc[j][ct] = f32x16{};
+  float m_use[kRB], l_run[kRB];
+#pragma unroll
+  for (int j = 0; j < kRB; ++j) {
+    m_use[j] = -INFINITY;
+    l_run[j] = 0.f;
+  }
 
   if (t_beg < t_end) {
-    // query row as the B operand
-    u32x4 qf[S::kSteps];
-    const unsigned short* qrow = (const unsigned short*)p.q + out_row * D;
+    // query rows as the B operand
+    u32x4 qf[kRB][S::kSteps];
 #pragma unroll
-    for (int kc = 0; kc < S::kSteps; ++kc)
-      qf[kc] = valid ? *(const u32x4*)(qrow + 16 * kc + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < kRB; ++j) {
+      const unsigned short* qrow = (const unsigned short*)p.q + out_row[j] * D;
+#pragma unroll
+      for (int kc = 0; kc < S::kSteps; ++kc)
+        qf[j][kc] = valid[j] ? *(const u32x4*)(qrow + 16 * kc + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
+    }
 
     // per-lane copy offsets: lane fills LDS bytes 16 lane .. +15 of each 1-KiB
     // piece u, i.e. row u * kRowsPerLoad + lane / kChunks, physical chunk
@@ -269,7 +302,6 @@ __global__ void __launch_bounds__(kWaves * kWaveSize) decode_split_kernel(Decode
     const int v_row_lane = 4 * hh + (gi >> 2);
     const int v_col_lane = 16 * (g16 & 1) + 4 * (gi & 3);
     const float c = p.scale_log2;
-    const unsigned span = (unsigned)(hi - lo);
     unsigned short* my = &smem[wave][0][0][0];
 
     // prologue: the first kStages - 1 tiles
@@ -279,13 +311,13 @@ __global__ void __launch_bounds__(kWaves * kWaveSize) decode_split_kernel(Decode
                                       my + (2 * j + 1) * S::kTileElems);
 
     for (int t = t_beg; t < t_end; ++t) {
-      const int j = t - t_beg;
-      const int st = j % kStages;
+      const int jt = t - t_beg;
+      const int st = jt % kStages;
       const unsigned short* kC = my + (2 * st) * S::kTileElems;
       const unsigned short* vC = my + (2 * st + 1) * S::kTileElems;
       // refill the stage read in the previous step (its reads are done)
       if (t + kStages - 1 < t_end) {
-        const int sn = (j + kStages - 1) % kStages;
+        const int sn = (jt + kStages - 1) % kStages;
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         K::issue(p, b, hk, L, t + kStages - 1, ok_, ov_, my + (2 * sn) * S::kTileElems,
                  my + (2 * sn + 1) * S::kTileElems);
@@ -294,50 +326,59 @@ __global__ void __launch_bounds__(kWaves * kWaveSize) decode_split_kernel(Decode
         wait_loads<0>();
       }
 
-      // scores S^T = K Q^T for keys 32t .. 32t+31
-      f32x16 sacc = f32x16{};
+      // scores S^T = K Q^T for keys 32t .. 32t+31; each K read serves every
+      // row block
+      f32x16 sacc[kRB];
+#pragma unroll
+      for (int j = 0; j < kRB; ++j) sacc[j] = f32x16{};
 #pragma unroll
       for (int kc = 0; kc < S::kSteps; ++kc) {
         const u32x4 a = *(const u32x4*)(kC + k_off<D>(l32, 2 * kc + hh));
-        sacc = E::mma(a, qf[kc], sacc);
+#pragma unroll
+        for (int j = 0; j < kRB; ++j) sacc[j] = E::mma(a, qf[j][kc], sacc[j]);
       }
-      // mask: key kb + 8(e/4) + 4hh + e%4 is visible iff lo <= key <= hi
-      const int base = t * kTile + 4 * hh - lo;
+      u32x4 pf[kRB][2];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int off = 8 * (e >> 2) + (e & 3);
-        sacc[e] = (any && (unsigned)(base + off) <= span) ? sacc[e] : -INFINITY;
+      for (int j = 0; j < kRB; ++j) {
+        // mask: key kb + 8(e/4) + 4hh + e%4 is visible iff lo <= key <= hi
+        const int base = t * kTile + 4 * hh - lo[j];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int off = 8 * (e >> 2) + (e & 3);
+          sacc[j][e] = (any[j] && (unsigned)(base + off) <= span[j]) ? sacc[j][e] : -INFINITY;
+        }
+        // online softmax (base 2, scale folded into the exponent)
+        float mx = sacc[j][0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[j][e]);
+        float mlo, mhi;
+        half_pair(mx, mlo, mhi);
+        mx = fmaxf(mlo, mhi) * c;
+        const bool bump = mx > m_use[j] + kRescaleSlack;
+        const float alpha = bump ? __builtin_amdgcn_exp2f(m_use[j] - mx) : 1.f;
+        m_use[j] = bump ? mx : m_use[j];
+        const float m_exp = (m_use[j] == -INFINITY) ? 0.f : m_use[j];
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          sacc[j][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][e], c, -m_exp));
+          part[e & 3] += sacc[j][e];
+        }
+        l_run[j] = __builtin_fmaf(l_run[j], alpha, (part[0] + part[1]) + (part[2] + part[3]));
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+          for (int ct = 0; ct < S::kOutTiles; ++ct) oacc[j][ct] *= alpha;
+        }
+#pragma unroll
+        for (int mc = 0; mc < 2; ++mc)
+          pf[j][mc] = u32x4{E::pack2(sacc[j][8 * mc + 0], sacc[j][8 * mc + 1]),
+                            E::pack2(sacc[j][8 * mc + 2], sacc[j][8 * mc + 3]),
+                            E::pack2(sacc[j][8 * mc + 4], sacc[j][8 * mc + 5]),
+                            E::pack2(sacc[j][8 * mc + 6], sacc[j][8 * mc + 7])};
       }
-      // online softmax (base 2, scale folded into the exponent)
-      float mx = sacc[0];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
-      float mlo, mhi;
-      half_pair(mx, mlo, mhi);
-      mx = fmaxf(mlo, mhi) * c;
-      const bool bump = mx > m_use + kRescaleSlack;
-      const float alpha = bump ? __builtin_amdgcn_exp2f(m_use - mx) : 1.f;
-      m_use = bump ? mx : m_use;
-      const float m_exp = (m_use == -INFINITY) ? 0.f : m_use;
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        sacc[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], c, -m_exp));
-        part[e & 3] += sacc[e];
-      }
-      l_run = __builtin_fmaf(l_run, alpha, (part[0] + part[1]) + (part[2] + part[3]));
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-        for (int ct = 0; ct < S::kOutTiles; ++ct) oacc[ct] *= alpha;
-      }
-      u32x4 pf[2];
-#pragma unroll
-      for (int mc = 0; mc < 2; ++mc)
-        pf[mc] = u32x4{E::pack2(sacc[8 * mc + 0], sacc[8 * mc + 1]), E::pack2(sacc[8 * mc + 2], sacc[8 * mc + 3]),
-                       E::pack2(sacc[8 * mc + 4], sacc[8 * mc + 5]), E::pack2(sacc[8 * mc + 6], sacc[8 * mc + 7])};
       // O^T += V^T P^T; k-step mc covers keys 16mc .. 16mc+15 in the
       // accumulator's order (half-wave hh holds 16mc + 4hh + {0..3} and
-      // 16mc + 8 + 4hh + {0..3})
+      // 16mc + 8 + 4hh + {0..3}); each V read serves every row block
 #pragma unroll
       for (int ct = 0; ct < S::kOutTiles; ++ct) {
         const int col = 32 * ct + v_col_lane;
@@ -346,7 +387,9 @@ __global__ void __launch_bounds__(kWaves * kWaveSize) decode_split_kernel(Decode
           const int ra = 16 * mc + v_row_lane;
           const u32x2 lo2 = __builtin_bit_cast(u32x2, lds_read_tr(vC, v_off<D>(ra, col)));
           const u32x2 hi2 = __builtin_bit_cast(u32x2, lds_read_tr(vC, v_off<D>(ra + 8, col)));
-          oacc[ct] = E::mma(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, pf[mc], oacc[ct]);
+          const u32x4 vt = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+#pragma unroll
+          for (int j = 0; j < kRB; ++j) oacc[j][ct] = E::mma(vt, pf[j][mc], oacc[j][ct]);
         }
       }
     }
@@ -354,38 +397,41 @@ __global__ void __launch_bounds__(kWaves * kWaveSize) decode_split_kernel(Decode
 
   // epilogue: this split's normalised output and logsumexp (o = 0 and
   // lse = -inf where the row saw no key)
-  float llo, lhi;
-  half_pair(l_run, llo, lhi);
-  const float l_tot = llo + lhi;
-  if (!valid) return;
-  const bool seen = l_tot > 0.f;
-  const float inv = seen ? 1.f / l_tot : 0.f;
-  const float lse = seen ? (m_use + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-  if (p.n_splits == 1) {
-    unsigned short* og = (unsigned short*)p.o + out_row * D;
 #pragma unroll
-    for (int ct = 0; ct < S::kOutTiles; ++ct) {
+  for (int j = 0; j < kRB; ++j) {
+    float llo, lhi;
+    half_pair(l_run[j], llo, lhi);
+    const float l_tot = llo + lhi;
+    if (!valid[j]) continue;
+    const bool seen = l_tot > 0.f;
+    const float inv = seen ? 1.f / l_tot : 0.f;
+    const float lse = seen ? (m_use[j] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    if (p.n_splits == 1) {
+      unsigned short* og = (unsigned short*)p.o + out_row[j] * D;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const u32x2 w = u32x2{E::pack2(oacc[ct][4 * gq + 0] * inv, oacc[ct][4 * gq + 1] * inv),
-                              E::pack2(oacc[ct][4 * gq + 2] * inv, oacc[ct][4 * gq + 3] * inv)};
-        *(u32x2*)(og + 32 * ct + 8 * gq + 4 * hh) = w;
+      for (int ct = 0; ct < S::kOutTiles; ++ct) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const u32x2 w = u32x2{E::pack2(oacc[j][ct][4 * gq + 0] * inv, oacc[j][ct][4 * gq + 1] * inv),
+                                E::pack2(oacc[j][ct][4 * gq + 2] * inv, oacc[j][ct][4 * gq + 3] * inv)};
+          *(u32x2*)(og + 32 * ct + 8 * gq + 4 * hh) = w;
+        }
       }
-    }
-    if (hh == 0 && p.lse != nullptr) p.lse[out_row] = lse;
-  } else {
-    const long long prow = (long long)s * p.rows + out_row;
-    float* po = p.part_o + prow * D;
+      if (hh == 0 && p.lse != nullptr) p.lse[out_row[j]] = lse;
+    } else {
+      const long long prow = (long long)s * p.rows + out_row[j];
+      float* po = p.part_o + prow * D;
 #pragma unroll
-    for (int ct = 0; ct < S::kOutTiles; ++ct) {
+      for (int ct = 0; ct < S::kOutTiles; ++ct) {
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const float4 w = make_float4(oacc[ct][4 * gq + 0] * inv, oacc[ct][4 * gq + 1] * inv,
-                                     oacc[ct][4 * gq + 2] * inv, oacc[ct][4 * gq + 3] * inv);
-        *(float4*)(po + 32 * ct + 8 * gq + 4 * hh) = w;
+        for (int gq = 0; gq < 4; ++gq) {
+          const float4 w = make_float4(oacc[j][ct][4 * gq + 0] * inv, oacc[j][ct][4 * gq + 1] * inv,
+                                       oacc[j][ct][4 * gq + 2] * inv, oacc[j][ct][4 * gq + 3] * inv);
+          *(float4*)(po + 32 * ct + 8 * gq + 4 * hh) = w;
+        }
       }
+      if (hh == 0) p.part_lse[prow] = lse;
     }
-    if (hh == 0) p.part_lse[prow] = lse;
   }
 }
 
@@ -449,14 +495,23 @@ __global__ void __launch_bounds__(kMergeRows * kWaveSize) decode_merge_kernel(De
   if (lane == 0 && p.lse != nullptr) p.lse[row] = l > 0.f ? mx + __logf(l) : -INFINITY;
 }
 
+template <typename E, int D, int kRB>
+void launch_split(const DecodeParams& p, int blocks, hipStream_t stream) {
+  if (p.block_table)
+    hipLaunchKernelGGL((decode_split_kernel<E, D, true, kRB>), dim3(blocks), dim3(kWaves * kWaveSize), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<E, D, false, kRB>), dim3(blocks), dim3(kWaves * kWaveSize), 0, stream,
+                       p);
+}
+
 template <typename E, int D>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-  const int units = p.total_items / p.n_row_blocks;
-  const int blocks = kWaves == 1 ? 8 * ((units + 7) / 8) * p.n_row_blocks : (p.total_items + kWaves - 1) / kWaves;
-  if (p.block_table)
-    hipLaunchKernelGGL((decode_split_kernel<E, D, true>), dim3(blocks), dim3(kWaves * kWaveSize), 0, stream, p);
+  const int units = p.total_items / p.n_row_items;
+  const int blocks = kWaves == 1 ? 8 * ((units + 7) / 8) * p.n_row_items : (p.total_items + kWaves - 1) / kWaves;
+  if (p.rb_per_item == 2)
+    launch_split<E, D, 2>(p, blocks, stream);
   else
-    hipLaunchKernelGGL((decode_split_kernel<E, D, false>), dim3(blocks), dim3(kWaves * kWaveSize), 0, stream, p);
+    launch_split<E, D, 1>(p, blocks, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
   const long long mblocks = (p.rows + kMergeRows - 1) / kMergeRows;
@@ -473,5 +528,7 @@ hipError_t launch_decode(const DecodeParams& p, int d, bool f16, hipStream_t str
 }
 
 int decode_waves_per_workgroup() { return kWaves; }
+
+int decode_row_blocks_per_item(int n_row_blocks) { return n_row_blocks >= 2 && kMaxRowBlocks >= 2 ? 2 : 1; }
 
 }  // namespace fa

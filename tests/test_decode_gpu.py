@@ -70,6 +70,8 @@ SHAPES = [
     (8, 1, 5, 64, [64, 32, 3, 5]),        # G * Nq = 40: two row blocks
     (32, 8, 16, 600, [600, 17, 300, 33]),  # G * Nq = 64
     (2, 2, 40, 130, [130, 40, 41, 128]),   # Nq > 32 on its own
+    (8, 1, 12, 200, [200, 150, 13, 0]),    # G * Nq = 96: a wavefront with one full and one empty block
+    (16, 1, 9, 160, [160, 31, 9, 100]),    # G * Nq = 144: five blocks, the last partly filled
 ]
 
 
