@@ -261,11 +261,13 @@ int fa_fwd_kvcache_num_splits(int B, int Hq, int Hkv, int Nq, int Nk);
  * num_splits together with the same lengths on the device).  Since a split
  * covers a fixed share of the capacity, short sequences leave their last
  * splits empty; this counts the splits that will read keys and takes the
- * fewest that give about three streaming wavefronts per compute unit while
- * keeping every work item in one wave of the grid (at most four per unit),
- * else the most splits within that wave, at least four 32-key tiles per
- * split and at most 128.  Equal full lengths give fewer splits than
- * fa_fwd_kvcache_num_splits when three streams per unit already suffice.
+ * fewest that give about three streaming wavefronts per compute unit (four
+ * when a GQA group's G * Nq query rows exceed 32, so that one wavefront
+ * takes two 32-row blocks) while keeping every work item in one wave of the
+ * grid (at most four per unit), else the fewest splits that put the most
+ * work items in that wave; at least four 32-key tiles per split and at most
+ * 128.  Equal full lengths give fewer splits than fa_fwd_kvcache_num_splits
+ * when three streams per unit already suffice.
  * Returns 1 for sizes that compute nothing or a null pointer. */
 int fa_fwd_kvcache_num_splits_for_lengths(int B, int Hq, int Hkv, int Nq, int Nk, int causal,
                                           int window_left, const int *cache_seqlens_host);
