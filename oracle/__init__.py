@@ -22,7 +22,9 @@ Contents
 ``attention_bwd_ref``  fp64 gradients dQ, dK, dV of the forward above for an
                    upstream gradient dO (chain rule through O = P V and the
                    row softmax; P rebuilt per block of rows), with optional
-                   absolute-value products for error bounds.
+                   absolute-value products for error bounds; and the same
+                   for packed sequences of different lengths (each
+                   sequence's queries aligned to the end of its keys).
 
 What is computed (all three): for batch b, query head h with key/value head
 h_kv = h // (Hq // Hkv), and query row i,
@@ -47,12 +49,14 @@ Every function here is pinned by tests in ``tests/test_oracle.py`` against
 closed forms, invariants, hand-worked fixtures and an independent library
 routine (torch's CPU scaled-dot-product attention in float64); the gradients
 are pinned in ``tests/test_oracle_bwd.py`` against central finite differences
-of the forward oracle, torch's float64 autograd, and closed forms; the cache
+of the forward oracle, torch's float64 autograd, and closed forms (the
+packed form against central finite differences of the packed forward oracle
+and against the fixed-length gradients sequence by sequence); the cache
 form in ``tests/test_oracle_kvcache.py`` against the last rows of the full
 forward oracle, a loop-by-loop brute force, and closed forms.
 """
 from .attention_ref import attention_fwd, masked, kv_head_of  # noqa: F401
 from .twopass_ref import attention_twopass  # noqa: F401
 from .online_emul import attention_online  # noqa: F401
-from .attention_bwd_ref import attention_bwd  # noqa: F401
+from .attention_bwd_ref import attention_bwd, attention_bwd_varlen  # noqa: F401
 from .attention_kvcache_ref import attention_fwd_kvcache, attention_fwd_varlen  # noqa: F401

@@ -45,29 +45,39 @@ from .attention_ref import kv_head_of, masked
 ROW_BLOCK = 256
 
 
-def _one_kv_head(qs, kh, vh, dos, causal, window_left, scale, bounds):
+def _one_kv_head(qs, kh, vh, dos, causal, window_left, scale, bounds, shift=0):
     """Gradients for one (batch, key/value head) and the query heads of its
-    group.  qs, dos: [G, N, d] fp64; kh, vh: [N, d] fp64.  Returns dq [G, N, d],
-    dk [N, d], dv [N, d] and, if bounds, a dict of magnitude terms."""
+    group.  qs, dos: [G, N, d] fp64; kh, vh: [Nk, d] fp64 (Nk = N for
+    self-attention).  Query row i stands at key position i + shift (0 for
+    self-attention; Nk - N when the queries are the last tokens of a longer
+    sequence); a row that sees no key has P = 0 and passes no gradient.
+    Returns dq [G, N, d], dk [Nk, d], dv [Nk, d] and, if bounds, a dict of
+    magnitude terms."""
     G, N, d = qs.shape
-    keys = np.arange(N)
+    Nk = kh.shape[0]
+    keys = np.arange(Nk)
     dq = np.zeros((G, N, d))
-    dk = np.zeros((N, d))
-    dv = np.zeros((N, d))
+    dk = np.zeros((Nk, d))
+    dv = np.zeros((Nk, d))
     mag = None
     if bounds:
-        mag = {"dq": np.zeros((G, N, d)), "dk": np.zeros((N, d)), "dv": np.zeros((N, d)),
-               "dq_f": np.zeros((G, N, d)), "dk_f": np.zeros((N, d))}
+        mag = {"dq": np.zeros((G, N, d)), "dk": np.zeros((Nk, d)), "dv": np.zeros((Nk, d)),
+               "dq_f": np.zeros((G, N, d)), "dk_f": np.zeros((Nk, d))}
+    if Nk == 0:
+        return dq, dk, dv, mag
     for g in range(G):
         qh, doh = qs[g], dos[g]
         for s0 in range(0, N, ROW_BLOCK):
             r = np.arange(s0, min(N, s0 + ROW_BLOCK))
+            pos = r + shift
             # recompute the probabilities of these rows against every key
             S = scale * (qh[r] @ kh.T)
-            S[masked(r[:, None], keys[None, :], causal, window_left)] = -np.inf
+            S[masked(pos[:, None], keys[None, :], causal, window_left)] = -np.inf
             m = S.max(axis=1, keepdims=True)
+            m[~np.isfinite(m)] = 0.0  # a row that sees no key: every E below is 0
             E = np.exp(S - m)
-            P = E / E.sum(axis=1, keepdims=True)
+            z = E.sum(axis=1, keepdims=True)
+            P = E / np.where(z > 0, z, 1.0)
             # chain rule through O = P V and the row softmax
             dv += P.T @ doh[r]
             dP = doh[r] @ vh.T
@@ -152,4 +162,73 @@ def attention_bwd(q, k, v, do, causal: bool = False, window_left: int = -1,
     else:
         with ThreadPoolExecutor(nthreads) as ex:
             list(ex.map(work, range(B * Hkv)))
+    return (dq, dk, dv, mags) if bounds else (dq, dk, dv)
+
+
+def attention_bwd_varlen(q, k, v, do, cu_seqlens_q, cu_seqlens_k, causal: bool = False, window_left: int = -1,
+                         scale: Optional[float] = None, threads: Optional[int] = None, bounds: bool = False):
+    """Gradients of ``attention_fwd_varlen`` (packed sequences) in float64.
+
+    q, do: [total_q, Hq, d]; k, v: [total_k, Hkv, d]; sequence b owns query
+    rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b]
+    .. cu_seqlens_k[b+1]-1, its Lq query rows standing at the end of its Lk
+    keys (row i at key position Lk - Lq + i).  Within each sequence this is
+    ``attention_bwd`` with that alignment; rows that see no key pass no
+    gradient.  Returns (dq [total_q, Hq, d], dk [total_k, Hkv, d],
+    dv [total_k, Hkv, d]), plus the magnitude terms (laid out like the
+    gradients) when bounds=True.
+    """
+    q, k, v, do = (np.asarray(x) for x in (q, k, v, do))
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = [int(x) for x in cu_seqlens_k]
+    if q.ndim != 3 or k.ndim != 3 or k.shape != v.shape or q.shape[2] != k.shape[2] or do.shape != q.shape:
+        raise ValueError("q, do must be [total_q, Hq, d] and k, v [total_k, Hkv, d]")
+    if len(cq) != len(ck) or len(cq) < 1 or cq[0] != 0 or ck[0] != 0 or cq[-1] != q.shape[0] \
+            or ck[-1] != k.shape[0] or any(b < a for a, b in zip(cq, cq[1:])) or any(b < a for a, b in zip(ck, ck[1:])):
+        raise ValueError("cu_seqlens must be nondecreasing prefix sums from 0 to the packed lengths")
+    Hq, d = q.shape[1], q.shape[2]
+    Hkv = k.shape[1]
+    if Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError("Hq must be a positive multiple of Hkv")
+    if window_left < -1:
+        raise ValueError("window_left must be >= -1")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    scale = float(scale)
+    dq = np.zeros((q.shape[0], Hq, d))
+    dk = np.zeros((k.shape[0], Hkv, d))
+    dv = np.zeros((k.shape[0], Hkv, d))
+    mags = None
+    if bounds:
+        mags = {"dq": np.zeros_like(dq), "dk": np.zeros_like(dk), "dv": np.zeros_like(dv),
+                "dq_f": np.zeros_like(dq), "dk_f": np.zeros_like(dk)}
+
+    def work(bk):
+        b, hk = divmod(bk, Hkv)
+        q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        heads = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == hk]
+        qs = np.stack([q[q0:q1, h].astype(np.float64) for h in heads])
+        dos = np.stack([do[q0:q1, h].astype(np.float64) for h in heads])
+        gq, gk, gv, mag = _one_kv_head(qs, k[k0:k1, hk].astype(np.float64), v[k0:k1, hk].astype(np.float64), dos,
+                                       causal, window_left, scale, bounds, shift=(k1 - k0) - (q1 - q0))
+        for gi, h in enumerate(heads):
+            dq[q0:q1, h] = gq[gi]
+            if bounds:
+                mags["dq"][q0:q1, h] = mag["dq"][gi]
+                mags["dq_f"][q0:q1, h] = mag["dq_f"][gi]
+        dk[k0:k1, hk] = gk
+        dv[k0:k1, hk] = gv
+        if bounds:
+            mags["dk"][k0:k1, hk] = mag["dk"]
+            mags["dv"][k0:k1, hk] = mag["dv"]
+            mags["dk_f"][k0:k1, hk] = mag["dk_f"]
+
+    n = (len(cq) - 1) * Hkv
+    nthreads = max(1, min(threads or len(os.sched_getaffinity(0)), max(n, 1)))
+    if nthreads == 1:
+        for bk in range(n):
+            work(bk)
+    else:
+        with ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(work, range(n)))
     return (dq, dk, dv, mags) if bounds else (dq, dk, dv)

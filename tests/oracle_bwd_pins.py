@@ -11,6 +11,12 @@ asserts a fact fixed by something other than the function itself:
   (sum_j dV_j = sum_i dO_i) and rows of dS sum to zero (sum_j dK_j = 0);
 - linearity in the upstream gradient and equivariance under a permutation of
   the keys (no mask).
+
+Pins for the packed-sequence gradients take bwd_varlen(q, k, v, do, cu_q,
+cu_k, causal=, window_left=, scale=): central finite differences of the
+packed forward oracle (sequences with fewer, as many and more queries than
+keys, rows that see no key, a sequence with no queries), and, for equal
+lengths, the fixed-length gradients above sequence by sequence.
 """
 from __future__ import annotations
 
@@ -18,7 +24,7 @@ import math
 
 import numpy as np
 
-from oracle import attention_fwd
+from oracle import attention_bwd, attention_fwd, attention_fwd_varlen
 from workloads import random_inputs
 
 MASKS = [(False, -1), (True, -1), (False, 0), (False, 3), (True, 0), (True, 2), (True, 5)]
@@ -176,3 +182,66 @@ def pin_bwd_key_permutation(bwd):
 
 ALL_BWD_PINS = [pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_equal_keys, pin_bwd_single_key,
                 pin_bwd_sum_rules, pin_bwd_linearity, pin_bwd_key_permutation]
+
+
+# ---------------------------------------------------------------------------
+# Packed sequences of different lengths
+
+def pin_varlen_bwd_finite_differences(bwd_varlen):
+    """dL/dx for L = sum(dO * O) of the packed forward oracle, by central
+    differences, element by element; query rows stand at the end of their
+    sequence's keys, and rows that see no key (more queries than keys under
+    a causal mask) have o = 0, so no gradient."""
+    lens = [(2, 4), (3, 3), (3, 1), (0, 2)]  # (queries, keys) per sequence
+    cq = np.cumsum([0] + [a for a, _ in lens])
+    ck = np.cumsum([0] + [b for _, b in lens])
+    Hq, Hkv, d = 2, 1, 3
+    rng = np.random.default_rng(470)
+    q = rng.standard_normal((cq[-1], Hq, d))
+    k = rng.standard_normal((ck[-1], Hkv, d))
+    v = rng.standard_normal((ck[-1], Hkv, d))
+    do = rng.standard_normal((cq[-1], Hq, d))
+    scale, h = 0.8, 1e-5
+    for causal, wl in [(False, -1), (True, -1), (True, 1), (False, 0)]:
+        def loss(qq, kk, vv):
+            o, _ = attention_fwd_varlen(qq, kk, vv, cq, ck, causal, wl, scale, threads=1)
+            return float((o * do).sum())
+        dq, dk, dv = bwd_varlen(q, k, v, do, cq, ck, causal=causal, window_left=wl, scale=scale)
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                args_p = {"q": q, "k": k, "v": v}
+                args_m = dict(args_p)
+                xp = x.copy()
+                xp[idx] += h
+                xm = x.copy()
+                xm[idx] -= h
+                args_p[name], args_m[name] = xp, xm
+                num[idx] = (loss(args_p["q"], args_p["k"], args_p["v"]) -
+                            loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * h)
+            np.testing.assert_allclose(g, num, rtol=0, atol=2e-8, err_msg=f"d{name} causal={causal} wl={wl}")
+
+
+def pin_varlen_bwd_equal_lengths(bwd_varlen):
+    """Equal query and key lengths: each sequence's gradients are the
+    fixed-length gradients of that sequence alone (GQA, every mask kind)."""
+    lens = [5, 1, 7, 3]
+    cu = np.cumsum([0] + lens)
+    Hq, Hkv, d = 4, 2, 4
+    rng = np.random.default_rng(471)
+    q = rng.standard_normal((cu[-1], Hq, d))
+    k = rng.standard_normal((cu[-1], Hkv, d))
+    v = rng.standard_normal((cu[-1], Hkv, d))
+    do = rng.standard_normal((cu[-1], Hq, d))
+    for causal, wl in MASKS:
+        dq, dk, dv = bwd_varlen(q, k, v, do, cu, cu, causal=causal, window_left=wl, scale=0.6)
+        for b in range(len(lens)):
+            a, z = cu[b], cu[b + 1]
+            per = lambda x: x[a:z].transpose(1, 0, 2)[None]  # noqa: E731  [1, H, L, d]
+            rq, rk, rv = attention_bwd(per(q), per(k), per(v), per(do), causal, wl, 0.6, threads=1)
+            for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+                np.testing.assert_allclose(got[a:z].transpose(1, 0, 2), ref[0], rtol=0, atol=1e-12,
+                                           err_msg=f"{name} sequence {b} causal={causal} wl={wl}")
+
+
+ALL_VARLEN_BWD_PINS = [pin_varlen_bwd_finite_differences, pin_varlen_bwd_equal_lengths]

@@ -8,7 +8,7 @@ import types
 import numpy as np
 import pytest
 
-from oracle import attention_bwd
+from oracle import attention_bwd, attention_bwd_varlen
 from tests import oracle_bwd_pins as pins
 from workloads import random_inputs
 
@@ -85,8 +85,8 @@ BWD_MUTANTS = [
     ("dV through Q", "dv += P.T @ doh[r]", "dv += P.T @ qh[r]"),
     ("dV from scores, not probabilities", "dv += P.T @ doh[r]", "dv += E.T @ doh[r]"),
     ("group sum dropped for dK", "dk += scale * (dS.T @ qh[r])", "dk = scale * (dS.T @ qh[r])"),
-    ("mask ignored in the backward", "S[masked(r[:, None], keys[None, :], causal, window_left)] = -np.inf",
-     "S[masked(r[:, None], keys[None, :], causal, window_left)] = S[masked(r[:, None], keys[None, :], causal, window_left)]"),
+    ("mask ignored in the backward", "S[masked(pos[:, None], keys[None, :], causal, window_left)] = -np.inf",
+     "S[masked(pos[:, None], keys[None, :], causal, window_left)] = S[masked(pos[:, None], keys[None, :], causal, window_left)]"),
     ("scores without the scale", "S = scale * (qh[r] @ kh.T)", "S = (qh[r] @ kh.T)"),
 ]
 
@@ -102,6 +102,52 @@ def test_bwd_pins_catch_planted_mistake(name, old, new):
     bwd = lambda q, k, v, do, c, w, s: mod.attention_bwd(q, k, v, do, c, w, s, threads=1)  # noqa: E731
     caught = []
     for pin in pins.ALL_BWD_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(bwd)
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake: {name}"
+
+
+# ---------------------------------------------------------------------------
+# Packed sequences of different lengths
+
+VARLEN_MUTANTS = [
+    ("queries aligned to the start of the keys", "pos = r + shift", "pos = r"),
+    ("rows that see no key divide by zero", "P = E / np.where(z > 0, z, 1.0)", "P = E / z"),
+    ("rows that see no key keep their max", "m[~np.isfinite(m)] = 0.0", "pass"),
+    ("dK of a sequence not scattered back", "dk[k0:k1, hk] = gk", "dk[k0:k1, hk] = 0 * gk"),
+]
+
+
+@pytest.mark.parametrize("pin", pins.ALL_VARLEN_BWD_PINS, ids=lambda f: f.__name__)
+def test_varlen_bwd_oracle_pin(pin):
+    pin(lambda *a, **kw: attention_bwd_varlen(*a, threads=1, **kw))
+
+
+def test_varlen_bwd_rejects_bad_arguments():
+    q = np.zeros((5, 2, 4))
+    k = np.zeros((7, 1, 4))
+    with pytest.raises(ValueError):
+        attention_bwd_varlen(q, k, k, q, [0, 2, 4], [0, 3, 7])  # q offsets stop short
+    with pytest.raises(ValueError):
+        attention_bwd_varlen(q, k, k, q, [0, 3, 5], [0, 4, 3, 7])
+    with pytest.raises(ValueError):
+        attention_bwd_varlen(q, k, k, q, [0, 3, 5], [0, 3, 7], window_left=-2)
+
+
+@pytest.mark.parametrize("name,old,new", VARLEN_MUTANTS, ids=[m[0] for m in VARLEN_MUTANTS])
+def test_varlen_bwd_pins_catch_planted_mistake(name, old, new):
+    path = os.path.join(ROOT, "oracle", "attention_bwd_ref.py")
+    src = open(path).read()
+    assert old in src, f"mutation anchor not found: {old!r}"
+    mod = types.ModuleType("oracle.bwd_varlen_mutant")
+    mod.__dict__["__package__"] = "oracle"
+    exec(compile(src.replace(old, new), "bwd_varlen_mutant", "exec"), mod.__dict__)
+    bwd = lambda *a, **kw: mod.attention_bwd_varlen(*a, threads=1, **kw)  # noqa: E731
+    caught = []
+    for pin in pins.ALL_VARLEN_BWD_PINS:
         try:
             with np.errstate(all="ignore"):
                 pin(bwd)
