@@ -10,7 +10,9 @@ of ``include/fa.h``).  This package is a thin binding:
                 ``fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, ...)``,
                 ``fwd_kvcache(q, k_cache, v_cache, cache_seqlens, ...)``,
                 ``fwd_kvcache_paged(q, k_pages, v_pages, block_table, ...)`` and
-                ``bwd(q, k, v, o, lse, dout, ...)`` on torch tensors, and
+                ``bwd(q, k, v, o, lse, dout, ...)``,
+                ``bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, ...)`` on
+                torch tensors, and
                 ``attend(q, k, v, ...)``, the forward as a differentiable
                 torch operation whose backward is ``bwd``
     build       compiles libfa.so in-tree with hipcc
@@ -53,10 +55,16 @@ def bwd(*args, **kwargs):
     return _bwd(*args, **kwargs)
 
 
+def bwd_varlen(*args, **kwargs):
+    from .attention import bwd_varlen as _f
+    return _f(*args, **kwargs)
+
+
 def attend(*args, **kwargs):
     from .attention import attend as _a
     return _a(*args, **kwargs)
 
 
-__all__ = ["fwd", "fwd_varlen", "fwd_fp8", "fwd_kvcache", "fwd_kvcache_paged", "kvcache_num_splits", "bwd", "attend", "FaError",
+__all__ = ["fwd", "fwd_varlen", "fwd_fp8", "fwd_kvcache", "fwd_kvcache_paged", "kvcache_num_splits", "bwd", "bwd_varlen",
+           "attend", "FaError",
            "LIB_PATH", "load"]

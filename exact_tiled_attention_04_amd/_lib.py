@@ -24,7 +24,7 @@ FA_ERR_HIP = -4
 
 EXPORTED = ["fa_fwd", "fa_fwd_bf16", "fa_fwd_f16", "fa_fwd_f32", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_kvcache",
             "fa_fwd_kvcache_paged", "fa_fwd_kvcache_num_splits", "fa_fwd_kvcache_num_splits_for_lengths",
-            "fa_fwd_kvcache_workspace_size", "fa_bwd",
+            "fa_fwd_kvcache_workspace_size", "fa_bwd", "fa_bwd_varlen",
             "fa_bwd_bf16", "fa_bwd_f16", "fa_bwd_workspace_size", "fa_status_string", "fa_last_error", "fa_version"]
 
 _lock = threading.Lock()
@@ -78,6 +78,8 @@ def load() -> ctypes.CDLL:
             fn.restype = I
         lib.fa_bwd.argtypes = bwd_args + [I]
         lib.fa_bwd.restype = I
+        lib.fa_bwd_varlen.argtypes = [P] * 12 + [I] * 10 + [F, P, I]
+        lib.fa_bwd_varlen.restype = I
         lib.fa_bwd_workspace_size.argtypes = [I, I, I]
         lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
         lib.fa_status_string.argtypes = [I]
@@ -161,6 +163,14 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, causa
     return load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                          _ptr(workspace), B, Hq, Hkv, N, d, int(bool(causal)), window_left, scale, _ptr(stream),
                          dtype)
+
+
+def fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q,
+                  total_k, max_seqlen_q, max_seqlen_k, d, causal, window_left, scale, stream, dtype) -> int:
+    return load().fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                                _ptr(dv), _ptr(workspace), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, Hq, Hkv,
+                                total_q, total_k, max_seqlen_q, max_seqlen_k, d, int(bool(causal)), window_left,
+                                scale, _ptr(stream), dtype)
 
 
 def fa_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, causal, window_left, scale,

@@ -324,6 +324,65 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
     return dq, dk, dv
 
 
+def bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+               dout: torch.Tensor, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
+               max_seqlen_k: int, causal: bool = False, window_left: int = -1, scale: Optional[float] = None,
+               dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+               dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Gradients of ``fwd_varlen``'s output with respect to q, k and v.
+
+    q, k, v, cu_seqlens_q/k, max_seqlen_q/k, causal, window_left, scale: as
+    passed to ``fwd_varlen``; o, lse: what it returned; dout: upstream
+    gradient like o.  Returns (dq, dk, dv) like (q, k, v); rows outside
+    every sequence are left as the given (or freshly allocated) tensors hold
+    them.  Asynchronous on ``stream``; raises _lib.FaError when the library
+    rejects the arguments."""
+    ts = (q, k, v, o, dout)
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or k.shape[2] != q.shape[2]:
+        raise ValueError("q must be [total_q, Hq, d] and k, v [total_k, Hkv, d]")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must be shaped like q")
+    if q.dtype not in (torch.float16, torch.bfloat16) or any(t.dtype != q.dtype for t in ts):
+        raise ValueError("q, k, v, o, dout must share one dtype, float16 or bfloat16")
+    if not q.is_cuda or any(t.device != q.device for t in ts + (lse,)):
+        raise ValueError("all tensors must be on one GPU")
+    if not all(t.is_contiguous() for t in ts + (lse,)):
+        raise ValueError("all tensors must be contiguous")
+    cq = _int32_dev(cu_seqlens_q, q.device, "cu_seqlens_q")
+    ck = _int32_dev(cu_seqlens_k, q.device, "cu_seqlens_k")
+    if cq is None or ck is None or cq.dim() != 1 or cq.shape != ck.shape or cq.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be int32 [B+1]")
+    total_q, Hq, d = q.shape
+    total_k, Hkv, _ = k.shape
+    if lse.shape != (Hq, total_q) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [Hq, total_q]")
+    B = cq.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = dq if dq is not None else torch.zeros_like(q)
+    dk = dk if dk is not None else torch.zeros_like(k)
+    dv = dv if dv is not None else torch.zeros_like(v)
+    for name, g, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if g.shape != ref.shape or g.dtype != ref.dtype or not g.is_contiguous() or g.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like its input")
+    nbytes = _lib.fa_bwd_workspace_size(1, Hq, total_q)
+    if workspace is None:
+        workspace = torch.empty(max(1, nbytes // 4), dtype=torch.float32, device=q.device)
+    if workspace.dtype != torch.float32 or workspace.numel() * 4 < nbytes or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous float32 tensor of at least {nbytes} bytes")
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        status = _lib.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                    workspace.data_ptr(), cq.data_ptr(), ck.data_ptr(), B, Hq, Hkv, total_q,
+                                    total_k, int(max_seqlen_q), int(max_seqlen_k), d, causal, window_left,
+                                    float(scale), s.cuda_stream, _DTYPES[q.dtype])
+    if status != _lib.FA_OK:
+        raise _lib.FaError(status, _lib.fa_last_error())
+    return dq, dk, dv
+
+
 class _Attention(torch.autograd.Function):
     """``fwd`` as a differentiable torch operation: the forward saves q, k, v,
     o and lse, the backward calls ``bwd`` with them."""

@@ -183,6 +183,87 @@ int run_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
   return FA_OK;
 }
 
+uint64_t bwd_workspace_bytes(int B, int Hq, int N);
+
+int run_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, float* work, const int* cu_q, const int* cu_k, int B, int Hq,
+                   int Hkv, int total_q, int total_k, int max_q, int max_k, int d, int causal, int window_left,
+                   float scale, void* stream, fa_dtype_t dtype) {
+  g_last_error[0] = '\0';
+  if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "the backward supports bf16 and fp16 only (dtype %d)", static_cast<int>(dtype));
+  if (B < 0 || Hq < 0 || Hkv < 0 || total_q < 0 || total_k < 0 || max_q < 0 || max_k < 0 || d < 0)
+    return fail(FA_ERR_INVALID_ARG, "negative size (B=%d Hq=%d Hkv=%d total_q=%d total_k=%d max_q=%d max_k=%d d=%d)",
+                B, Hq, Hkv, total_q, total_k, max_q, max_k, d);
+  if (B == 0 || Hq == 0 || total_q == 0 || max_q == 0) return FA_OK;
+  if (Hkv == 0 || Hq % Hkv != 0)
+    return fail(FA_ERR_INVALID_ARG, "Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
+  if (window_left < -1) return fail(FA_ERR_INVALID_ARG, "window_left=%d (must be -1 or >= 0)", window_left);
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale is not finite");
+  if (!(scale > 0.f)) return fail(FA_ERR_UNSUPPORTED, "scale=%g: only positive scales are supported", (double)scale);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d (supported: 64, 128)", d);
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !work || !cu_q || !cu_k)
+    return fail(FA_ERR_INVALID_ARG, "null pointer among q/k/v/o/lse/dout/dq/dk/dv/workspace/cu_seqlens");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(work, 16))
+    return fail(FA_ERR_MISALIGNED, "q, k, v, o, dout, dq, dk, dv and the workspace must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(cu_q, 4) || !aligned(cu_k, 4))
+    return fail(FA_ERR_MISALIGNED, "lse and cu_seqlens must be 4-byte aligned");
+  const uint64_t n_q = (uint64_t)total_q * Hq * d * 2;
+  const uint64_t n_kv = (uint64_t)total_k * Hkv * d * 2;
+  const uint64_t n_l = (uint64_t)Hq * total_q * sizeof(float);
+  const uint64_t n_w = bwd_workspace_bytes(1, Hq, total_q);
+  struct Span {
+    const void* p;
+    uint64_t n;
+  };
+  const Span outs[4] = {{dq, n_q}, {dk, n_kv}, {dv, n_kv}, {work, n_w}};
+  const Span all[10] = {{q, n_q}, {k, n_kv}, {v, n_kv}, {o, n_q}, {lse, n_l}, {dout, n_q},
+                        {dq, n_q}, {dk, n_kv}, {dv, n_kv}, {work, n_w}};
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 10; ++j)
+      if (j != 6 + i && overlap(outs[i].p, outs[i].n, all[j].p, all[j].n))
+        return fail(FA_ERR_INVALID_ARG, "an output (dq, dk, dv or the workspace) overlaps another buffer");
+  // one sequence's rows of one head are addressed with 32-bit byte offsets
+  if ((uint64_t)max_k * Hkv * d * 2 + (1u << 20) > (uint64_t)INT32_MAX ||
+      (uint64_t)max_q * Hq * d * 2 + (1u << 20) > (uint64_t)INT32_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "max_seqlen_q=%d / max_seqlen_k=%d too long (one sequence's rows must stay "
+                "below 2 GiB)", max_q, max_k);
+  const long long rows = fa::bwd_rows_per_workgroup();
+  const long long items_q = (long long)B * Hq * ((max_q + rows - 1) / rows);
+  const long long items_k = (long long)B * Hkv * ((max_k + rows - 1) / rows);
+  if (items_q > fa::kMaxGridItems || items_k > fa::kMaxGridItems || (long long)Hq * total_q / 16 > fa::kMaxGridItems)
+    return fail(FA_ERR_UNSUPPORTED, "too many sequences, heads or rows for one launch");
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.work = work;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.N = max_q;
+  a.d = d;
+  a.causal = causal;
+  a.window_left = window_left;
+  a.scale = scale;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  a.max_k = max_k;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_bwd_bf16(a, s) : fa::launch_bwd_f16(a, s);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
 int run_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale, float v_scale, void* o,
             float* lse, int B, int Hq, int Hkv, int N, int d, int causal, int window_left, float scale,
             void* stream) {
@@ -575,6 +656,14 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            int window_left, float scale, void* stream, fa_dtype_t dtype) {
   return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, causal, window_left, scale,
                  stream, dtype);
+}
+
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, float* workspace, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                  int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
+                  int causal, int window_left, float scale, void* stream, fa_dtype_t dtype) {
+  return run_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv,
+                        total_q, total_k, max_seqlen_q, max_seqlen_k, d, causal, window_left, scale, stream, dtype);
 }
 
 int fa_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

@@ -87,31 +87,35 @@ __device__ __forceinline__ int tr_off(int row, int col) {  // element offset of 
 
 // Per-lane source offsets of this lane's part of a tile copy: lane l fills
 // LDS bytes 16l..16l+15 of its 1-KiB piece, i.e. physical chunk l % kChunks
-// of its row, so it fetches the logical chunk the swizzle maps there.
+// of its row, so it fetches the logical chunk the swizzle maps there.  Rows
+// lie row_bytes apart in memory (2 D for one head's contiguous rows, more
+// for token-major packed sequences).
 template <int D, int W = kWaves>
 struct CopyOffsets {
   int off[Shape<D, W>::kLoadsPerWave];
-  __device__ __forceinline__ void init(int wave, int lane) {
+  int row_bytes;
+  __device__ __forceinline__ void init(int wave, int lane, int rb) {
     using S = Shape<D, W>;
+    row_bytes = rb;
 #pragma unroll
     for (int u = 0; u < S::kLoadsPerWave; ++u) {
       const int piece = wave * S::kLoadsPerWave + u;
       const int row = piece * S::kRowsPerLoad + lane / S::kChunks;
       const int pch = lane % S::kChunks;
-      off[u] = row * S::kRowBytes + ((pch ^ swz<D>(row)) << 4);
+      off[u] = row * rb + ((pch ^ swz<D>(row)) << 4);
     }
   }
 };
 
 // Copy rows row0 .. row0+kTile-1 of the tensor behind `r` (bounded to the
-// head's N rows: rows past the end arrive as zeros) straight into LDS.
+// head's rows: rows past the end arrive as zeros) straight into LDS.
 template <int D, int W = kWaves>
 __device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t r, const CopyOffsets<D, W>& c,
                                           unsigned short* dst, int row0, int wave) {
   using S = Shape<D, W>;
   // (builtin arguments go through plain ints: the host compilation pass
   // rejects template-dependent expressions in this builtin's operands)
-  const int soff = row0 * S::kRowBytes;
+  const int soff = row0 * c.row_bytes;
 #pragma unroll
   for (int u = 0; u < S::kLoadsPerWave; ++u) {
     const int piece = wave * S::kLoadsPerWave + u;
@@ -132,6 +136,33 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, lo
 
 // Wait for every copy this wave issued, then for every wave.
 __device__ __forceinline__ void barrier_all() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One sequence's rows and, for packed sequences, where they sit: query rows
+// qa .. qa+Nq-1 and key rows ka .. ka+Nk-1, query row i at key position
+// i + shift (shift = Nk - Nq: the queries are the sequence's last tokens).
+// Offsets are clamped to the packed tensors and lengths to the launch's
+// maxima, so inconsistent offsets never address outside the buffers.
+struct SeqRows {
+  int qa, ka, Nq, Nk, shift;
+};
+template <bool kPacked>
+__device__ __forceinline__ SeqRows seq_rows(const BwdParams& p, int b) {
+  SeqRows r;
+  if constexpr (kPacked) {
+    typedef __attribute__((address_space(4))) const int cint;
+    r.qa = min(max(((cint*)p.cu_q)[b], 0), p.total_q);
+    const int qz = min(max(((cint*)p.cu_q)[b + 1], r.qa), p.total_q);
+    r.ka = min(max(((cint*)p.cu_k)[b], 0), p.total_k);
+    const int kz = min(max(((cint*)p.cu_k)[b + 1], r.ka), p.total_k);
+    r.Nq = min(qz - r.qa, p.N);
+    r.Nk = min(kz - r.ka, p.max_k);
+  } else {
+    r.qa = r.ka = 0;
+    r.Nq = r.Nk = p.N;
+  }
+  r.shift = r.Nk - r.Nq;
+  return r;
+}
 
 // A = the streamed tile read through the transposing load for k-step mc
 // (rows 16mc..16mc+15 in the accumulator's order) and output tile ct.
@@ -222,7 +253,7 @@ __device__ __forceinline__ float dot8<F16>(u32x4 a, u32x4 b) {
   return s;
 }
 
-template <typename E, int D>
+template <typename E, int D, bool kPacked>
 __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
   constexpr int kLanesPerRow = D / 8;
   constexpr int kRowsPerBlock = 256 / kLanesPerRow;
@@ -237,8 +268,17 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
 #pragma unroll
   for (int m = kLanesPerRow / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, kLanesPerRow);
   if (row < p.rows && c == 0) {
-    p.delta[row] = s;
-    p.lse2[row] = p.lse[row] * kLog2e;
+    // packed: row = token * Hq + head, while lse and the row terms are
+    // [Hq][total_q]
+    long long idx = row;
+    if constexpr (kPacked) {
+      const long long t = row / p.Hq;
+      idx = (row - t * p.Hq) * p.total_q + t;
+    }
+    p.delta[idx] = s;
+    // a row that saw no key (lse = -inf) gets P = exp2(s - inf) = 0
+    const float l = p.lse[idx];
+    p.lse2[idx] = l == -INFINITY ? INFINITY : l * kLog2e;
   }
 }
 
@@ -294,7 +334,7 @@ __device__ __forceinline__ void scores_from_lds(const unsigned short* __restrict
   }
 }
 
-template <typename E, int D>
+template <typename E, int D, bool kPacked>
 __global__ void __launch_bounds__(kDkvThreads) bwd_dkdv_kernel(BwdParams p) {
   using S = Shape<D, kDkvWaves>;
   // Q and dO tiles (double-buffered) in one array: at the end its space holds
@@ -318,63 +358,84 @@ __global__ void __launch_bounds__(kDkvThreads) bwd_dkdv_kernel(BwdParams p) {
 
   // work item: heavy first (with a causal mask the first key blocks see the most queries)
   const int L = xcd_slice_index(blockIdx.x, p.items_dkv);
-  const int bk = L / p.n_blocks;
-  const int kb = L - bk * p.n_blocks;
+  const int bk = L / p.n_kblocks;
+  const int kb = L - bk * p.n_kblocks;
   const int b = bk / p.Hkv;
   const int hk = bk - b * p.Hkv;
-  const int N = p.N;
+  const SeqRows sr = seq_rows<kPacked>(p, b);
+  const int Nq = sr.Nq, Nk = sr.Nk, shift = sr.shift;
   const int k0 = kb * kBlock;
+  if (k0 >= Nk) return;  // the whole workgroup: past this sequence's keys
   const int kw0 = k0 + kg * kRows;
   const int myk = kw0 + l32;
-  const long long kv_head = ((long long)b * p.Hkv + hk) * N * D;
+  // element offset of this head's key row 0 and of its query heads' row 0,
+  // and the row strides (in elements) of K/V and of Q/dO
+  const int kv_rs = kPacked ? p.Hkv * D : D;
+  const int q_rs = kPacked ? p.Hq * D : D;
+  const long long kv_head =
+      kPacked ? ((long long)sr.ka * p.Hkv + hk) * D : ((long long)b * p.Hkv + hk) * (long long)Nk * D;
 
   u32x4 kf[kKvInLds<D> ? 1 : S::kSteps], vf[kKvInLds<D> ? 1 : S::kSteps];
   if (!kKvInLds<D>) {
-    load_own_row<D>((const unsigned short*)p.k + kv_head + (long long)myk * D, myk < N, hh, kf);
-    load_own_row<D>((const unsigned short*)p.v + kv_head + (long long)myk * D, myk < N, hh, vf);
+    load_own_row<D>((const unsigned short*)p.k + kv_head + (long long)myk * kv_rs, myk < Nk, hh, kf);
+    load_own_row<D>((const unsigned short*)p.v + kv_head + (long long)myk * kv_rs, myk < Nk, hh, vf);
   }
   f32x16 dk[S::kOutTiles], dv[S::kOutTiles];
 #pragma unroll
   for (int ct = 0; ct < S::kOutTiles; ++ct) dk[ct] = dv[ct] = f32x16{};
 
-  // queries that see some key of the block: causal from k0 on, a window up
-  // to the last key + window_left
+  // queries that see some key of the block (query i stands at key position
+  // i + shift): causal from key k0 on, a window up to the last key +
+  // window_left
   const int wl = p.window_left;
-  const int k_last = min(N - 1, k0 + kBlock - 1);
-  const int q_lo = p.causal ? k0 : 0;
-  const int q_hi = wl >= 0 ? min(N - 1, k_last + wl) : N - 1;
-  const int t_lo = q_lo / kTile, t_hi = q_hi / kTile;
-  const int n_t = t_hi - t_lo + 1;
+  const int k_last = min(Nk - 1, k0 + kBlock - 1);
+  const int q_lo = p.causal ? max(0, k0 - shift) : 0;
+  const int q_hi = wl >= 0 ? min(Nq - 1, k_last + wl - shift) : Nq - 1;
+  const int t_lo = q_lo / kTile;
+  const int n_t = q_hi >= q_lo ? q_hi / kTile - t_lo + 1 : 0;
   const int n_tiles = p.group * n_t;  // (query head in group, query tile)
 
   // visible queries of this lane's key form [vq_lo, vq_lo + vq_span]
-  const int vq_lo = myk < N ? (p.causal ? myk : 0) : 0x3fffffff;
-  const unsigned vq_span = myk < N ? (unsigned)((wl >= 0 ? min(N - 1, myk + wl) : N - 1) - vq_lo) : 0u;
-  const int wk_last = min(N - 1, kw0 + kRows - 1);
+  int vq_lo = 0x3fffffff;
+  unsigned vq_span = 0u;
+  if (myk < Nk) {
+    const int lo = p.causal ? max(0, myk - shift) : 0;
+    const int hi = wl >= 0 ? min(Nq - 1, myk + wl - shift) : Nq - 1;
+    if (hi >= lo) {
+      vq_lo = lo;
+      vq_span = (unsigned)(hi - lo);
+    }
+  }
+  const int wk_last = min(Nk - 1, kw0 + kRows - 1);
 
-  CopyOffsets<D, kDkvWaves> co;
-  co.init(wave, lane);
-  const int head_bytes = N * S::kRowBytes;
+  CopyOffsets<D, kDkvWaves> co;  // Q and dO rows
+  co.init(wave, lane, 2 * q_rs);
+  CopyOffsets<D, kDkvWaves> ck;  // K and V rows
+  ck.init(wave, lane, 2 * kv_rs);
+  const int q_bytes = Nq > 0 ? (Nq - 1) * 2 * q_rs + S::kRowBytes : 0;
+  const int kv_bytes = (Nk - 1) * 2 * kv_rs + S::kRowBytes;
   auto issue = [&](int tau, int buf) {
     const int g = tau / n_t;
     const int q0 = (t_lo + tau - g * n_t) * kTile;
-    const long long bh = (long long)b * p.Hq + hk * p.group + g;
-    copy_tile<D, kDkvWaves>(head_rsrc(p.q, 2 * bh * N * D, head_bytes), co, sQ[buf], q0, wave);
-    copy_tile<D, kDkvWaves>(head_rsrc(p.dout, 2 * bh * N * D, head_bytes), co, sO[buf], q0, wave);
-    if (wave == 0) copy_vec(head_rsrc(p.lse2, 4 * bh * N, 4 * N), sL[buf], q0, lane);
-    if (wave == 1) copy_vec(head_rsrc(p.delta, 4 * bh * N, 4 * N), sD[buf], q0, lane);
+    const long long hq = (long long)hk * p.group + g;
+    const long long qh0 = kPacked ? ((long long)sr.qa * p.Hq + hq) * D : ((long long)b * p.Hq + hq) * Nq * D;
+    const long long vh0 = kPacked ? hq * p.total_q + sr.qa : ((long long)b * p.Hq + hq) * Nq;
+    copy_tile<D, kDkvWaves>(head_rsrc(p.q, 2 * qh0, q_bytes), co, sQ[buf], q0, wave);
+    copy_tile<D, kDkvWaves>(head_rsrc(p.dout, 2 * qh0, q_bytes), co, sO[buf], q0, wave);
+    if (wave == 0) copy_vec(head_rsrc(p.lse2, 4 * vh0, 4 * Nq), sL[buf], q0, lane);
+    if (wave == 1) copy_vec(head_rsrc(p.delta, 4 * vh0, 4 * Nq), sD[buf], q0, lane);
   };
 
   if (kKvInLds<D>) {  // rows k0 .. k0+127 of K and V (zeros past the end)
 #pragma unroll
     for (int part = 0; part < kBlock / kTile; ++part) {
-      copy_tile<D, kDkvWaves>(head_rsrc(p.k, 2 * kv_head, head_bytes), co, sKk + part * kTile * D,
+      copy_tile<D, kDkvWaves>(head_rsrc(p.k, 2 * kv_head, kv_bytes), ck, sKk + part * kTile * D,
                               k0 + part * kTile, wave);
-      copy_tile<D, kDkvWaves>(head_rsrc(p.v, 2 * kv_head, head_bytes), co, sVk + part * kTile * D,
+      copy_tile<D, kDkvWaves>(head_rsrc(p.v, 2 * kv_head, kv_bytes), ck, sVk + part * kTile * D,
                               k0 + part * kTile, wave);
     }
   }
-  issue(0, 0);
+  if (n_tiles > 0) issue(0, 0);
   barrier_all();
   const float c = p.scale_log2;
   for (int tau = 0; tau < n_tiles; ++tau) {
@@ -383,10 +444,11 @@ __global__ void __launch_bounds__(kDkvThreads) bwd_dkdv_kernel(BwdParams p) {
     const int g = tau / n_t;
     const int qs = (t_lo + tau - g * n_t) * kTile + 32 * qh;  // first query of this wave's half
     // skip the half when no (query, key) pair of this wavefront is visible
-    const bool any = kw0 < N && qs < N && !(p.causal && qs + 31 < kw0) && !(wl >= 0 && qs > wk_last + wl);
+    const bool any = kw0 < Nk && qs < Nq && !(p.causal && qs + 31 + shift < kw0) &&
+                     !(wl >= 0 && qs + shift > wk_last + wl);
     if (any) {
-      const bool need_mask = qs + 32 > N || kw0 + kRows > N || (p.causal && qs < kw0 + kRows - 1) ||
-                             (wl >= 0 && qs + 31 > kw0 + wl);
+      const bool need_mask = qs + 32 > Nq || kw0 + kRows > Nk || (p.causal && qs + shift < kw0 + kRows - 1) ||
+                             (wl >= 0 && qs + 31 + shift > kw0 + wl);
       f32x16 s, dp;  // S[query][key], dP[query][key]
       if constexpr (kKvInLds<D>) {
         scores_from_lds<E, D>(sQ[buf], sO[buf], sKk, sVk, kg * kRows, qh, l32, hh, s, dp);
@@ -467,16 +529,16 @@ __global__ void __launch_bounds__(kDkvThreads) bwd_dkdv_kernel(BwdParams p) {
   };
   exchange(dk);
   exchange(dv);
-  if (qh == 0 && myk < N) {
-    store_row<E, D>((unsigned short*)p.dk + kv_head + (long long)myk * D, dk, p.scale, hh);
-    store_row<E, D>((unsigned short*)p.dv + kv_head + (long long)myk * D, dv, 1.f, hh);
+  if (qh == 0 && myk < Nk) {
+    store_row<E, D>((unsigned short*)p.dk + kv_head + (long long)myk * kv_rs, dk, p.scale, hh);
+    store_row<E, D>((unsigned short*)p.dv + kv_head + (long long)myk * kv_rs, dv, 1.f, hh);
   }
 }
 
 // ---------------------------------------------------------------------------
 // 3. dQ: workgroup = (batch, query head, 128 queries), as in the forward.
 
-template <typename E, int D>
+template <typename E, int D, bool kPacked>
 __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p) {
   using S = Shape<D>;
   __shared__ __attribute__((aligned(16))) unsigned short sK[2][kTile * D];
@@ -498,39 +560,57 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p) {
   const int hg = w - qrank * p.group;
   const int b = gidx / p.Hkv;
   const int hk = gidx - b * p.Hkv;
-  const long long bh = (long long)b * p.Hq + hk * p.group + hg;
+  const long long hq = (long long)hk * p.group + hg;
   const int qb = p.causal ? (p.n_blocks - 1 - qrank) : qrank;
-  const int N = p.N;
+  const SeqRows sr = seq_rows<kPacked>(p, b);
+  const int Nq = sr.Nq, Nk = sr.Nk, shift = sr.shift;
   const int q0 = qb * kBlock;
+  if (q0 >= Nq) return;  // the whole workgroup: past this sequence's rows
   const int wq0 = q0 + wave * kRows;
   const int myq = wq0 + l32;
-  const long long q_head = bh * N * D;
-  const long long kv_head = ((long long)b * p.Hkv + hk) * N * D;
+  // element offsets of this head's row 0, row strides in elements, and the
+  // offset of its row terms
+  const int q_rs = kPacked ? p.Hq * D : D;
+  const int kv_rs = kPacked ? p.Hkv * D : D;
+  const long long q_head = kPacked ? ((long long)sr.qa * p.Hq + hq) * D : ((long long)b * p.Hq + hq) * Nq * D;
+  const long long kv_head =
+      kPacked ? ((long long)sr.ka * p.Hkv + hk) * D : ((long long)b * p.Hkv + hk) * (long long)Nk * D;
+  const long long vec0 = kPacked ? hq * p.total_q + sr.qa : ((long long)b * p.Hq + hq) * Nq;
 
   u32x4 qf[S::kSteps], of[S::kSteps];
-  load_own_row<D>((const unsigned short*)p.q + q_head + (long long)myq * D, myq < N, hh, qf);
-  load_own_row<D>((const unsigned short*)p.dout + q_head + (long long)myq * D, myq < N, hh, of);
-  const float l2 = myq < N ? p.lse2[bh * N + myq] : INFINITY;  // rows past the end: P = 0
-  const float dd = myq < N ? p.delta[bh * N + myq] : 0.f;
+  load_own_row<D>((const unsigned short*)p.q + q_head + (long long)myq * q_rs, myq < Nq, hh, qf);
+  load_own_row<D>((const unsigned short*)p.dout + q_head + (long long)myq * q_rs, myq < Nq, hh, of);
+  const float l2 = myq < Nq ? p.lse2[vec0 + myq] : INFINITY;  // rows past the end: P = 0
+  const float dd = myq < Nq ? p.delta[vec0 + myq] : 0.f;
   f32x16 dq[S::kOutTiles];
 #pragma unroll
   for (int ct = 0; ct < S::kOutTiles; ++ct) dq[ct] = f32x16{};
 
-  // key tiles this workgroup needs, and this lane's visible keys
+  // key tiles this workgroup needs (query i stands at key position
+  // i + shift), and this lane's visible keys [vis_lo, vis_lo + vis_span]
   const int wl = p.window_left;
-  const int kend = p.causal ? min(N, q0 + kBlock) : N;
-  const int kbeg = wl >= 0 ? max(0, q0 - wl) : 0;
-  const int t_beg = kbeg / kTile, t_end = (kend + kTile - 1) / kTile;
-  const int vis_lo = wl >= 0 ? max(0, myq - wl) : 0;
-  const unsigned vis_span = (unsigned)((p.causal ? min(myq, N - 1) : N - 1) - vis_lo);
-  const int wq1 = min(N, wq0 + kRows) - 1;
+  const int kend = p.causal ? min(Nk, q0 + kBlock + shift) : Nk;
+  const int kbeg = wl >= 0 ? max(0, q0 + shift - wl) : 0;
+  const int t_beg = kbeg / kTile, t_end = kend > kbeg ? (kend + kTile - 1) / kTile : t_beg;
+  int vis_lo = 0x3fffffff;
+  unsigned vis_span = 0u;
+  if (myq < Nq) {
+    const int pos = myq + shift;
+    const int lo = wl >= 0 ? max(0, pos - wl) : 0;
+    const int hi = p.causal ? min(pos, Nk - 1) : Nk - 1;
+    if (hi >= lo) {
+      vis_lo = lo;
+      vis_span = (unsigned)(hi - lo);
+    }
+  }
+  const int wq1 = min(Nq, wq0 + kRows) - 1;
 
   CopyOffsets<D> co;
-  co.init(wave, lane);
-  const int head_bytes = N * S::kRowBytes;
+  co.init(wave, lane, 2 * kv_rs);
+  const int kv_bytes = Nk > 0 ? (Nk - 1) * 2 * kv_rs + S::kRowBytes : 0;
   auto issue = [&](int t, int buf) {
-    copy_tile<D>(head_rsrc(p.k, 2 * kv_head, head_bytes), co, sK[buf], t * kTile, wave);
-    copy_tile<D>(head_rsrc(p.v, 2 * kv_head, head_bytes), co, sV[buf], t * kTile, wave);
+    copy_tile<D>(head_rsrc(p.k, 2 * kv_head, kv_bytes), co, sK[buf], t * kTile, wave);
+    copy_tile<D>(head_rsrc(p.v, 2 * kv_head, kv_bytes), co, sV[buf], t * kTile, wave);
   };
 
   if (t_beg < t_end) issue(t_beg, 0);
@@ -539,9 +619,10 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p) {
     const int buf = (t - t_beg) & 1;
     if (t + 1 < t_end) issue(t + 1, buf ^ 1);
     const int kb = t * kTile;
-    const bool any = wq0 < N && !(p.causal && kb > wq1) && !(wl >= 0 && kb + kTile - 1 < wq0 - wl);
+    const bool any = wq0 < Nq && !(p.causal && kb > wq1 + shift) && !(wl >= 0 && kb + kTile - 1 < wq0 + shift - wl);
     if (any) {
-      const bool need_mask = kb + kTile > N || (p.causal && kb + kTile - 1 > wq0) || (wl >= 0 && kb < wq1 - wl);
+      const bool need_mask = kb + kTile > Nk || (p.causal && kb + kTile - 1 > wq0 + shift) ||
+                             (wl >= 0 && kb < wq1 + shift - wl);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const f32x16 s = rows_times_own<E, D>(sK[buf], h, l32, hh, qf);   // S^T[key][query]
@@ -569,18 +650,23 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p) {
     }
     barrier_all();
   }
-  if (myq < N) store_row<E, D>((unsigned short*)p.dq + q_head + (long long)myq * D, dq, p.scale, hh);
+  if (myq < Nq) store_row<E, D>((unsigned short*)p.dq + q_head + (long long)myq * q_rs, dq, p.scale, hh);
+}
+
+template <typename E, int D, bool kPacked>
+hipError_t launch_t(const BwdParams& p, hipStream_t stream) {
+  constexpr int kRowsPerPrepBlock = 256 / (D / 8);
+  const long long prep_blocks = (p.rows + kRowsPerPrepBlock - 1) / kRowsPerPrepBlock;
+  hipLaunchKernelGGL((bwd_prep_kernel<E, D, kPacked>), dim3((unsigned)prep_blocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kPacked>), dim3(p.items_dkv), dim3(kDkvThreads), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D, kPacked>), dim3(p.items_dq), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
 }
 
 template <typename E, int D>
 hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   const BwdParams p = make_bwd_params(a, kBlock);
-  constexpr int kRowsPerPrepBlock = 256 / (D / 8);
-  const long long prep_blocks = (p.rows + kRowsPerPrepBlock - 1) / kRowsPerPrepBlock;
-  hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)prep_blocks), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D>), dim3(p.items_dkv), dim3(kDkvThreads), 0, stream, p);
-  hipLaunchKernelGGL((bwd_dq_kernel<E, D>), dim3(p.items_dq), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  return a.cu_q ? launch_t<E, D, true>(p, stream) : launch_t<E, D, false>(p, stream);
 }
 
 }  // namespace

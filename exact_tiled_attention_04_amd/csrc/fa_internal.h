@@ -127,11 +127,16 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* work;  // 2 * B * Hq * N floats: row terms D_i, then lse_i * log2(e)
-  int B, Hq, Hkv, N, d;
+  float* work;  // 2 * B * Hq * N floats (packed: 2 * Hq * total_q): row terms D_i, then lse_i * log2(e)
+  int B, Hq, Hkv, N, d;  // packed sequences: N = max_seqlen_q
   int causal;
   int window_left;
   float scale;
+  // packed variable-length sequences (null: fixed N), as FwdArgs: q, o, dout,
+  // dq [total_q][Hq][d], k, v, dk, dv [total_k][Hkv][d], lse [Hq][total_q]
+  const int* cu_q = nullptr;
+  const int* cu_k = nullptr;
+  int total_q = 0, total_k = 0, max_k = 0;
 };
 
 struct BwdParams {
@@ -144,18 +149,22 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // [B][Hq][N]: sum_c dout * o
-  float* lse2;   // [B][Hq][N]: lse * log2(e)
-  long long rows;  // B * Hq * N
-  int B, Hq, Hkv, N;
+  float* delta;  // [B][Hq][N] (packed: [Hq][total_q]): sum_c dout * o
+  float* lse2;   // same layout: lse * log2(e), +inf where lse = -inf
+  long long rows;  // B * Hq * N (packed: Hq * total_q)
+  int B, Hq, Hkv, N;  // packed: N = max_seqlen_q
   int group;
   int causal;
-  int window_left;   // -1 = none (normalised: >= N-1 becomes -1)
-  int n_blocks;      // ceil(N / 128): query blocks (dQ) or key blocks (dK/dV)
+  int window_left;   // -1 = none (normalised: a window reaching key 0 from every row becomes -1)
+  int n_blocks;      // ceil(N / 128): query blocks (dQ)
+  int n_kblocks;     // key blocks (dK/dV): ceil(N / 128), packed ceil(max_seqlen_k / 128)
   int items_dq;      // B * Hq * n_blocks
-  int items_dkv;     // B * Hkv * n_blocks
+  int items_dkv;     // B * Hkv * n_kblocks
   float scale;
   float scale_log2;
+  const int* cu_q;   // packed sequences, as BwdArgs (null: fixed N)
+  const int* cu_k;
+  int total_q, total_k, max_k;
 };
 
 inline BwdParams make_bwd_params(const BwdArgs& a, int rows_per_wg) {
@@ -169,7 +178,8 @@ inline BwdParams make_bwd_params(const BwdArgs& a, int rows_per_wg) {
   p.dq = a.dq;
   p.dk = a.dk;
   p.dv = a.dv;
-  p.rows = (long long)a.B * a.Hq * a.N;
+  const bool packed = a.cu_q != nullptr;
+  p.rows = packed ? (long long)a.Hq * a.total_q : (long long)a.B * a.Hq * a.N;
   p.delta = a.work;
   p.lse2 = a.work + p.rows;
   p.B = a.B;
@@ -178,12 +188,22 @@ inline BwdParams make_bwd_params(const BwdArgs& a, int rows_per_wg) {
   p.N = a.N;
   p.group = a.Hq / a.Hkv;
   p.causal = a.causal ? 1 : 0;
-  p.window_left = (a.window_left >= a.N - 1) ? -1 : a.window_left;
+  // a row at key position pos sees keys from pos - window_left on: with
+  // positions below the key count, a window of that many keys or more
+  // reaches key 0 from every row
+  const int nk = packed ? a.max_k : a.N;
+  p.window_left = (a.window_left >= nk - 1) ? -1 : a.window_left;
   p.n_blocks = (a.N + rows_per_wg - 1) / rows_per_wg;
+  p.n_kblocks = (nk + rows_per_wg - 1) / rows_per_wg;
   p.items_dq = a.B * a.Hq * p.n_blocks;
-  p.items_dkv = a.B * a.Hkv * p.n_blocks;
+  p.items_dkv = a.B * a.Hkv * p.n_kblocks;
   p.scale = a.scale;
   p.scale_log2 = a.scale * 1.4426950408889634f;
+  p.cu_q = a.cu_q;
+  p.cu_k = a.cu_k;
+  p.total_q = a.total_q;
+  p.total_k = a.total_k;
+  p.max_k = a.max_k;
   return p;
 }
 

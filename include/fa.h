@@ -323,8 +323,39 @@ int fa_bwd_f16(const void *q, const void *k, const void *v, const void *o, const
                int B, int Hq, int Hkv, int N, int d, int causal, int window_left,
                float scale, void *stream);
 
+/*
+ * Gradients of fa_fwd_varlen's output: the fa_bwd operation within each
+ * packed sequence, with fa_fwd_varlen's layouts, offsets and alignment (query
+ * row i of sequence b at key position Lk - Lq + i; the causal mask and window
+ * measured from there).
+ *
+ *   q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q,
+ *   total_k, max_seqlen_q, max_seqlen_k, d, causal, window_left, scale
+ *                as given to (and returned by) fa_fwd_varlen; lse is
+ *                required.  Rows that saw no key (lse = -inf) pass no
+ *                gradient.
+ *   dout         [total_q][Hq][d], element type of q.
+ *   dq           [total_q][Hq][d]; dk, dv [total_k][Hkv][d].  Rows of every
+ *                sequence up to max_seqlen_q queries and max_seqlen_k keys are
+ *                written (keys no query sees get 0); rows outside every
+ *                sequence are left as they were.
+ *   workspace    device memory of fa_bwd_workspace_size(1, Hq, total_q)
+ *                bytes, 16-byte aligned, as for fa_bwd.
+ *   stream, dtype  as for fa_bwd.
+ *
+ * Offsets are clamped into range as in fa_fwd_varlen, so inconsistent ones
+ * give unspecified values, never an access outside the tensors.  Overlap
+ * rules, errors, reproducibility and ownership as for fa_bwd; one sequence's
+ * rows of all heads must stay below 2 GiB (max_seqlen * H * d * 2 bytes).
+ */
+int fa_bwd_varlen(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                  const void *dout, void *dq, void *dk, void *dv, float *workspace,
+                  const int *cu_seqlens_q, const int *cu_seqlens_k, int B, int Hq, int Hkv,
+                  int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
+                  int causal, int window_left, float scale, void *stream, fa_dtype_t dtype);
+
 /* Bytes of workspace fa_bwd needs: 2 * B * Hq * N * sizeof(float) (0 when
- * any size is 0 or negative). */
+ * any size is 0 or negative); fa_bwd_varlen takes B = 1, N = total_q. */
 size_t fa_bwd_workspace_size(int B, int Hq, int N);
 
 /* Static, human-readable name of a status code (never NULL). */

@@ -365,3 +365,47 @@ def test_varlen_f32_and_empty():
     assert call_vl(B=0, q=0, k=0, v=0, o=0, lse=0, cq=0, ck=0) == _lib.FA_OK
     assert call_vl(tq=0) == _lib.FA_OK
     assert call_vl(mq=0) == _lib.FA_OK
+
+
+# packed variable-length backward: fake addresses (1 MiB apart; the sizes
+# below keep every buffer inside its MiB)
+GOOD_BVL = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, work=W, cq=CQ, ck=CK, B=2, Hq=4, Hkv=2,
+                tq=40, tk=50, mq=30, mk=30, d=64, causal=1, window_left=-1, scale=0.125, stream=None)
+
+
+def call_bvl(dtype=_lib.FA_DTYPE_BF16, **over):
+    a = dict(GOOD_BVL, **over)
+    return _lib.fa_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"],
+                              a["work"], a["cq"], a["ck"], a["B"], a["Hq"], a["Hkv"], a["tq"], a["tk"], a["mq"],
+                              a["mk"], a["d"], a["causal"], a["window_left"], a["scale"], a["stream"], dtype)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(B=-1), _lib.FA_ERR_INVALID_ARG),
+    (dict(tk=-1), _lib.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), _lib.FA_ERR_INVALID_ARG),
+    (dict(window_left=-2), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), _lib.FA_ERR_UNSUPPORTED),
+    (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
+    (dict(lse=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(work=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(cq=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(ck=CK + 2), _lib.FA_ERR_MISALIGNED),
+    (dict(dq=DQ + 8), _lib.FA_ERR_MISALIGNED),
+    (dict(dk=DV), _lib.FA_ERR_INVALID_ARG),
+    (dict(dq=Q), _lib.FA_ERR_INVALID_ARG),
+    (dict(work=L), _lib.FA_ERR_INVALID_ARG),
+    (dict(mk=2 ** 24), _lib.FA_ERR_UNSUPPORTED),
+    (dict(mq=2 ** 23), _lib.FA_ERR_UNSUPPORTED),
+])
+def test_bwd_varlen_validation_rejects(over, status):
+    assert call_bvl(**over) == status
+    assert _lib.fa_last_error() != ""
+
+
+def test_bwd_varlen_f32_and_empty():
+    assert call_bvl(dtype=_lib.FA_DTYPE_F32) == _lib.FA_ERR_UNSUPPORTED
+    assert call_bvl(B=0, q=0, k=0, v=0, o=0, lse=0, dout=0, dq=0, dk=0, dv=0, work=0, cq=0, ck=0) == _lib.FA_OK
+    assert call_bvl(tq=0) == _lib.FA_OK
+    assert call_bvl(mq=0) == _lib.FA_OK
