@@ -22,7 +22,8 @@ decoding workload), as algorithmic bytes per second against HBM bandwidth.
 
 ``--varlen`` times the packed variable-length forward on
 ``varlen_causal_16`` (16 sequences of 512-8192 tokens), FLOPs over the exact
-visible pairs of every sequence.
+visible pairs of every sequence; ``--varlen --bwd`` its backward (one step =
+one ``fa.bwd_varlen`` call, credited 2.5 x those FLOPs).
 
 ``--matrix-ceiling`` times the vendor bf16 GEMM (torch.matmul, hipBLASLt) on
 square 8192^3 and 16384^3 products, once with inputs drawn like the headline
@@ -543,6 +544,98 @@ def run_varlen(args, name, with_cpu):
     return rec
 
 
+def run_varlen_bwd(args, name, with_cpu):
+    """Packed sequences of different lengths, backward: one step = one
+    fa.bwd_varlen call (dq, dk, dv from the forward's o and lse, which are
+    computed once before the timed region).  Credited work is 2.5 times the
+    forward's metric FLOPs (the five products of the backward against the
+    forward's two), the convention of the batched backward line."""
+    import numpy as np
+    import torch
+
+    import exact_tiled_attention_04_amd as fa
+    import workloads as W
+
+    w = W.VARLEN_WORKLOADS[name]
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    q, k, v, cu = W.make_varlen_inputs(w)
+    do = W.random_grad(w.seed + 100, w.dtype, 1, w.Hq, q.shape[0], w.d)[0].transpose(1, 0, 2)
+    qd, kd, vd = (torch.from_numpy(x).to(tdt).cuda() for x in (q, k, v))
+    dod = torch.from_numpy(np.ascontiguousarray(do)).to(tdt).cuda()
+    cud = torch.from_numpy(cu).cuda()
+    maxlen = int(np.diff(cu).max())
+    o, lse = fa.fwd_varlen(qd, kd, vd, cud, cud, maxlen, maxlen, causal=w.causal, window_left=w.window_left,
+                           scale=w.scale)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    ws = torch.empty(max(1, fa._lib.fa_bwd_workspace_size(1, w.Hq, q.shape[0]) // 4), dtype=torch.float32,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fa.bwd_varlen(qd, kd, vd, o, lse, dod, cud, cud, maxlen, maxlen, causal=w.causal,
+                      window_left=w.window_left, scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream)
+
+    wall, per_launch_ms = time_steps(step, args, name, stream)
+    avg_ms = float(np.mean(per_launch_ms))
+    flops = 2.5 * W.varlen_metric_flops(w, cu)
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    rec = {
+        "metric": "attention bwd TFLOP/s + % of MI355X bf16 MFMA peak (packed sequences of different lengths)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "lengths": [int(x) for x in np.diff(cu)],
+                   "total_tokens": int(cu[-1]), "d": w.d, "causal": w.causal, "window_left": w.window_left,
+                   "scale": w.scale, "seed": w.seed, "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "bwd_prep + bwd_dkdv + bwd_dq (packed)",
+                     "avg_call_us": round(avg_ms * 1e3, 2),
+                     "min_call_us": round(float(np.min(per_launch_ms)) * 1e3, 2)},
+    }
+    if with_cpu:
+        print(f"[bench] {name}: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline_varlen_bwd(w, q, k, v, do, cu)
+    return rec
+
+
+def cpu_baseline_varlen_bwd(w, q, k, v, do, cu, budget_s: float = 12.0):
+    """The fp64 packed gradient oracle, as it stands, on a bounded sample:
+    whole sequences from the first until ``budget_s`` of wall time has
+    passed; credited like the GPU line (2.5 x the forward's FLOPs)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import workloads as W
+    from oracle import attention_bwd_varlen
+
+    cores = len(os.sched_getaffinity(0))
+    done, flops = 0, 0.0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while done < w.B and time.perf_counter() - t0 < budget_s:
+            a, z = int(cu[done]), int(cu[done + 1])
+            sub = np.array([0, z - a], dtype=np.int32)
+            attention_bwd_varlen(q[a:z], k[a:z], v[a:z], do[a:z], sub, sub, w.causal, w.window_left, w.scale,
+                                 threads=cores)
+            flops += 2.5 * W.varlen_metric_flops(w, sub)
+            done += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": min(cores, w.Hkv), "kind": "oracle",
+            "sample": f"{done} of {w.B} sequences (every head and row), fp64 numpy, {dt:.1f} s wall"}
+
+
 def run_matrix_ceiling(args):
     """bf16 GEMM throughput of the vendor library on inputs like the headline
     workload's (0.5 * N(0, 1), rounded to bf16) and on zeros, one JSON line
@@ -594,7 +687,8 @@ def main():
                     help="time attention against a key/value cache (workload decode_gqa_32k, or --workload)")
     ap.add_argument("--splits", type=int, default=None, help="--decode: split count (default: the library's)")
     ap.add_argument("--varlen", action="store_true",
-                    help="time the packed variable-length forward (workload varlen_causal_16)")
+                    help="time the packed variable-length forward (workload varlen_causal_16; with --bwd its "
+                         "backward)")
     ap.add_argument("--matrix-ceiling", action="store_true",
                     help="time the vendor bf16 GEMM on headline-like data and on zeros (reference)")
     args = ap.parse_args()
@@ -614,7 +708,8 @@ def main():
         return
     if args.varlen:
         name = args.workload if args.workload in W.VARLEN_WORKLOADS else "varlen_causal_16"
-        print(json.dumps(run_varlen(args, name, not args.no_cpu_baseline)), flush=True)
+        runner = run_varlen_bwd if args.bwd else run_varlen
+        print(json.dumps(runner(args, name, not args.no_cpu_baseline)), flush=True)
         return
     if args.decode:
         names = sorted(W.DECODE_WORKLOADS) if args.all else \

@@ -230,8 +230,10 @@ int run_bwd_varlen(const void* q, const void* k, const void* v, const void* o, c
     return fail(FA_ERR_UNSUPPORTED, "max_seqlen_q=%d / max_seqlen_k=%d too long (one sequence's rows must stay "
                 "below 2 GiB)", max_q, max_k);
   const long long rows = fa::bwd_rows_per_workgroup();
-  const long long items_q = (long long)B * Hq * ((max_q + rows - 1) / rows);
-  const long long items_k = (long long)B * Hkv * ((max_k + rows - 1) / rows);
+  // the launches round the (sequence, key/value head) groups up to a multiple of 8
+  const long long groups8 = 8 * (((long long)B * Hkv + 7) / 8);
+  const long long items_q = groups8 * (Hq / Hkv) * ((max_q + rows - 1) / rows);
+  const long long items_k = groups8 * ((max_k + rows - 1) / rows);
   if (items_q > fa::kMaxGridItems || items_k > fa::kMaxGridItems || (long long)Hq * total_q / 16 > fa::kMaxGridItems)
     return fail(FA_ERR_UNSUPPORTED, "too many sequences, heads or rows for one launch");
   fa::BwdArgs a;

@@ -357,9 +357,22 @@ __global__ void __launch_bounds__(kDkvThreads) bwd_dkdv_kernel(BwdParams p) {
   const int row_lane = 4 * hh + (gi >> 2), col_lane = 16 * (g16 & 1) + 4 * (gi & 3);
 
   // work item: heavy first (with a causal mask the first key blocks see the most queries)
-  const int L = xcd_slice_index(blockIdx.x, p.items_dkv);
-  const int bk = L / p.n_kblocks;
-  const int kb = L - bk * p.n_kblocks;
+  int bk, kb;
+  if constexpr (kPacked) {
+    // sequences of different lengths cost very different amounts: XCD x
+    // (workgroup id mod 8) takes the (sequence, key/value head) groups x,
+    // x + 8, ..., each with all its key blocks, heaviest first; the grid
+    // holds 8 * ceil(groups / 8) groups and the missing ones return at once
+    const int r = blockIdx.x / 8;
+    const int j = r / p.n_kblocks;
+    kb = r - j * p.n_kblocks;
+    bk = 8 * j + blockIdx.x % 8;
+    if (bk >= p.B * p.Hkv) return;
+  } else {
+    const int L = xcd_slice_index(blockIdx.x, p.items_dkv);
+    bk = L / p.n_kblocks;
+    kb = L - bk * p.n_kblocks;
+  }
   const int b = bk / p.Hkv;
   const int hk = bk - b * p.Hkv;
   const SeqRows sr = seq_rows<kPacked>(p, b);
@@ -551,11 +564,22 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p) {
   const int g16 = lane >> 4, gi = lane & 15;
   const int row_lane = 4 * hh + (gi >> 2), col_lane = 16 * (g16 & 1) + 4 * (gi & 3);
 
-  // work item: the forward's order (causal: last query block first)
-  const int L = xcd_slice_index(blockIdx.x, p.items_dq);
+  // work item: the forward's order (causal: last query block first);
+  // packed sequences deal the (sequence, key/value head) groups round-robin
+  // over the XCDs as in the dK/dV kernel
   const int per_group = p.group * p.n_blocks;
-  const int gidx = L / per_group;
-  const int w = L - gidx * per_group;
+  int gidx, w;
+  if constexpr (kPacked) {
+    const int r = blockIdx.x / 8;
+    const int j = r / per_group;
+    w = r - j * per_group;
+    gidx = 8 * j + blockIdx.x % 8;
+    if (gidx >= p.B * p.Hkv) return;
+  } else {
+    const int L = xcd_slice_index(blockIdx.x, p.items_dq);
+    gidx = L / per_group;
+    w = L - gidx * per_group;
+  }
   const int qrank = w / p.group;
   const int hg = w - qrank * p.group;
   const int b = gidx / p.Hkv;
@@ -658,8 +682,12 @@ hipError_t launch_t(const BwdParams& p, hipStream_t stream) {
   constexpr int kRowsPerPrepBlock = 256 / (D / 8);
   const long long prep_blocks = (p.rows + kRowsPerPrepBlock - 1) / kRowsPerPrepBlock;
   hipLaunchKernelGGL((bwd_prep_kernel<E, D, kPacked>), dim3((unsigned)prep_blocks), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kPacked>), dim3(p.items_dkv), dim3(kDkvThreads), 0, stream, p);
-  hipLaunchKernelGGL((bwd_dq_kernel<E, D, kPacked>), dim3(p.items_dq), dim3(kThreads), 0, stream, p);
+  // packed: the grids hold 8 * ceil(groups / 8) (sequence, key/value head) groups
+  const long long groups8 = 8 * (((long long)p.B * p.Hkv + 7) / 8);
+  const long long g_dkv = kPacked ? groups8 * p.n_kblocks : p.items_dkv;
+  const long long g_dq = kPacked ? groups8 * p.group * p.n_blocks : p.items_dq;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kPacked>), dim3((unsigned)g_dkv), dim3(kDkvThreads), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D, kPacked>), dim3((unsigned)g_dq), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
