@@ -30,6 +30,13 @@
 //      forward's layout: each wavefront owns 32 queries, 64-key tiles of K and
 //      V stream through LDS.
 //
+// Packed sequences of different lengths (kPacked) run the same kernels with
+// per-sequence offsets and lengths, token-major rows ([token][head][d], so
+// row strides of H * d elements) and each sequence's queries standing at the
+// end of its keys (query i at key position i + Lk - Lq); the row terms and
+// lse are [Hq][total_q].  A row that sees no key has lse = -inf and gets
+// P = 0 everywhere.
+//
 // Matrix-core mapping as in the forward (v_mfma_f32_32x32x16; lane l holds
 // A[l%32][8*(l/32)+j], B[8*(l/32)+j][l%32], C[8*(i/4)+4*(l/32)+i%4][l%32]):
 // every product keeps the wavefront's own rows on the accumulator columns, so
