@@ -13,8 +13,9 @@ of ``include/fa.h``).  This package is a thin binding:
                 ``bwd(q, k, v, o, lse, dout, ...)``,
                 ``bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, ...)`` on
                 torch tensors, and
-                ``attend(q, k, v, ...)``, the forward as a differentiable
-                torch operation whose backward is ``bwd``
+                ``attend(q, k, v, ...)`` / ``attend_varlen(...)``, the
+                forwards as differentiable torch operations whose backwards
+                are ``bwd`` / ``bwd_varlen``
     build       compiles libfa.so in-tree with hipcc
 """
 from ._lib import FaError, LIB_PATH, load  # noqa: F401
@@ -60,11 +61,16 @@ def bwd_varlen(*args, **kwargs):
     return _f(*args, **kwargs)
 
 
+def attend_varlen(*args, **kwargs):
+    from .attention import attend_varlen as _a
+    return _a(*args, **kwargs)
+
+
 def attend(*args, **kwargs):
     from .attention import attend as _a
     return _a(*args, **kwargs)
 
 
 __all__ = ["fwd", "fwd_varlen", "fwd_fp8", "fwd_kvcache", "fwd_kvcache_paged", "kvcache_num_splits", "bwd", "bwd_varlen",
-           "attend", "FaError",
+           "attend", "attend_varlen", "FaError",
            "LIB_PATH", "load"]

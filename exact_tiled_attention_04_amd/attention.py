@@ -411,3 +411,37 @@ def attend(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fal
     """
     o, _ = _Attention.apply(q, k, v, causal, window_left, scale)
     return o
+
+
+class _AttentionVarlen(torch.autograd.Function):
+    """``fwd_varlen`` as a differentiable torch operation: the forward saves
+    q, k, v, o, lse and the offsets, the backward calls ``bwd_varlen``."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal, window_left, scale):
+        o, lse = fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal=causal,
+                            window_left=window_left, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k)
+        ctx.args = (max_seqlen_q, max_seqlen_k, causal, window_left, scale)
+        ctx.mark_non_differentiable(lse)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, dout, _dlse):
+        q, k, v, o, lse, cq, ck = ctx.saved_tensors
+        max_q, max_k, causal, window_left, scale = ctx.args
+        dq, dk, dv = bwd_varlen(q, k, v, o, lse, dout.contiguous(), cq, ck, max_q, max_k, causal=causal,
+                                window_left=window_left, scale=scale)
+        return dq, dk, dv, None, None, None, None, None, None, None
+
+
+def attend_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                  cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, causal: bool = False,
+                  window_left: int = -1, scale: Optional[float] = None) -> torch.Tensor:
+    """Differentiable attention over packed sequences: returns o like
+    ``fwd_varlen`` and, under backpropagation, the gradients of q, k and v
+    from ``bwd_varlen`` (rows outside every sequence get zero gradients).
+    cu_seqlens_q/k must be int32 tensors on q's GPU."""
+    o, _ = _AttentionVarlen.apply(q, k, v, cu_seqlens_q, cu_seqlens_k, int(max_seqlen_q), int(max_seqlen_k), causal,
+                                  window_left, scale)
+    return o

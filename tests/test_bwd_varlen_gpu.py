@@ -113,3 +113,23 @@ def test_bwd_varlen_rows_outside_every_sequence_are_untouched():
     assert (got[0][cq[-1]:] == 3.0).all() and (got[1][ck[-1]:] == 3.0).all() and (got[2][ck[-1]:] == 3.0).all()
     check(tuple(g[:int(c[-1])] for g, c in zip(got, (cq, ck, ck))), q[:cq[-1]], k[:ck[-1]], v[:ck[-1]],
           do[:cq[-1]], cq, ck, True, -1, 0.1, "f16", "extra rows")
+
+
+def test_differentiable_packed_attention_matches_fwd_and_bwd():
+    """fa.attend_varlen under torch autograd gives the same bits as calling
+    fwd_varlen and bwd_varlen directly."""
+    lq, lk = [40, 0, 130, 7], [60, 5, 130, 3]
+    q, k, v, do, cq, ck = _draw(1760, "bf16", lq, lk, 4, 2, 64)
+    ref = run(q, k, v, do, cq, ck, True, 25, 0.12, "bf16", "autograd reference")
+    qd, kd, vd = (to_dev(x, "bf16").requires_grad_() for x in (q, k, v))
+    dod = to_dev(do, "bf16")
+    cqd, ckd = torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda()
+    announce("autograd packed attention")
+    o = fa.attend_varlen(qd, kd, vd, cqd, ckd, max(lq), max(lk), causal=True, window_left=25, scale=0.12)
+    o_direct, _ = fa.fwd_varlen(qd.detach(), kd.detach(), vd.detach(), cqd, ckd, max(lq), max(lk), causal=True,
+                                window_left=25, scale=0.12)
+    (o * dod).sum().backward()
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o_direct)
+    for t, r in zip((qd, kd, vd), ref):
+        np.testing.assert_array_equal(t.grad.double().cpu().numpy(), r)
