@@ -385,8 +385,8 @@ int run_kvcache(const void* q, const void* k, const void* v, const int* block_ta
   if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale is not finite");
   if (!(scale > 0.f)) return fail(FA_ERR_UNSUPPORTED, "scale=%g: only positive scales are supported", (double)scale);
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d (supported: 64, 128)", d);
-  if (paged && page_size % 32 != 0)
-    return fail(FA_ERR_UNSUPPORTED, "page_size=%d must be a multiple of 32", page_size);
+  if (paged && page_size != 16 && page_size % 32 != 0)
+    return fail(FA_ERR_UNSUPPORTED, "page_size=%d must be 16 or a multiple of 32", page_size);
   const long long cap = paged ? (long long)page_size * max_pages : (long long)Nk;
   if (cap > INT32_MAX / 2) return fail(FA_ERR_UNSUPPORTED, "cache capacity of %lld keys is too large", cap);
   if (!q || !k || !v || !o) return fail(FA_ERR_INVALID_ARG, "null q/k/v/o pointer");

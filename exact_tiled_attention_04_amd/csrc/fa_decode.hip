@@ -36,7 +36,8 @@
 // Two cache layouts share the kernel: a contiguous cache [B][Hkv][Nk][d]
 // with per-batch lengths, and a paged cache [pages][page_size][Hkv][d] with a
 // per-batch table of page indices (page_size a multiple of 32, so a tile never
-// straddles two pages).  Page indices outside [0, pages) read as zeros.
+// straddles two pages, or 16, when each half of a tile comes from its own
+// page).  Page indices outside [0, pages) read as zeros.
 #include "fa_internal.h"
 #include "fa_decode.h"
 #include "fa_mfma_common.h"
@@ -169,10 +170,54 @@ struct Decode {
     return r;
   }
 
+  // 16-token pages: the buffer of the page holding keys 16 slot ..
+  // 16 slot + 15 (slot = 2t + half), based 16 half rows before the page so
+  // that the tile's row offsets (rows 16 half .. 16 half + 15) address it,
+  // and bounded to the sequence's rows of the page (offsets below 16 half
+  // rows are never used).  A slot past the sequence reads no table entry.
+  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t half_src(const DecodeParams& p, const void* base,
+                                                                   int b, int hk, int L, int slot, int half) {
+    const int row_bytes = p.row_stride * 2;
+    const bool live = slot * 16 < L;  // then slot < max_pages, as L <= 16 * max_pages
+    const int page = live ? scalar_load(p.block_table, (long long)b * p.max_pages + slot) : -1;
+    const bool ok = page >= 0 && page < p.num_pages;
+    const int rows = min(16, L - slot * 16);
+    const char* pb = (const char*)base + ((long long)(ok ? page : 0) * 16 * p.row_stride + (long long)hk * D) * 2 -
+                     (long long)half * 16 * row_bytes;
+    const int bytes = ok && rows > 0 ? half * 16 * row_bytes + (rows - 1) * row_bytes + S::kRowBytes : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)pb, 0, bytes, kBufferFlags);
+  }
+
   // Start copying tile t of K and V into LDS (2 * kLoads loads per lane).
   static __device__ __forceinline__ void issue(const DecodeParams& p, int b, int hk, int L, int t,
                                                const int* ok_, const int* ov_, unsigned short* kdst,
                                                unsigned short* vdst) {
+    if constexpr (kPaged) {
+      if (p.page_size < kTile) {
+        // load u covers rows u * kRowsPerLoad ..: the first kLoads / 2 loads
+        // are the tile's first 16 rows
+        static_assert(S::kLoads % 2 == 0 && S::kRowsPerLoad <= 16, "a load must stay within one half tile");
+        __amdgpu_buffer_rsrc_t kr[2], vr[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          kr[h] = half_src(p, p.k, b, hk, L, 2 * t + h, h);
+          vr[h] = half_src(p, p.v, b, hk, L, 2 * t + h, h);
+        }
+#pragma unroll
+        for (int u = 0; u < S::kLoads; ++u) {
+          const int o = ok_[u];
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(kr[u >= S::kLoads / 2], (lds_void_t*)(kdst + u * 512), 16, o, 0,
+                                                   0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < S::kLoads; ++u) {
+          const int o = ov_[u];
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vr[u >= S::kLoads / 2], (lds_void_t*)(vdst + u * 512), 16, o, 0,
+                                                   0, 0);
+        }
+        return;
+      }
+    }
     const TileSrc ks = tile_src(p, p.k, b, hk, L, t);
     const TileSrc vs = tile_src(p, p.v, b, hk, L, t);
 #pragma unroll

@@ -240,7 +240,7 @@ int fa_fwd_kvcache(const void *q, const void *k_cache, const void *v_cache,
  *                 [0, num_pages) reads as zeros (never out of bounds).
  *   cache_seqlens device int32 [B], required, in [0, page_size *
  *                 max_pages_per_seq] (clamped).
- *   page_size     a multiple of 32.
+ *   page_size     16 or a multiple of 32.
  *   Everything else as fa_fwd_kvcache, with Nk = page_size * max_pages_per_seq
  *   for the workspace size.
  */

@@ -252,7 +252,8 @@ def test_kvcache_paged_validation():
         return _lib.fa_fwd_kvcache_paged(a["q"], a["k"], a["v"], a["bt"], a["seq"], a["o"], a["lse"], a["ws"],
                                          a["B"], a["Hq"], a["Hkv"], a["Nq"], a["d"], a["pages"], a["ps"], a["maxp"],
                                          a["causal"], a["wl"], a["scale"], a["splits"], None, _lib.FA_DTYPE_BF16)
-    assert call(ps=48) == _lib.FA_ERR_UNSUPPORTED         # page size not a multiple of 32
+    assert call(ps=48) == _lib.FA_ERR_UNSUPPORTED         # page size neither 16 nor a multiple of 32
+    assert call(ps=8) == _lib.FA_ERR_UNSUPPORTED
     assert call(ps=0) == _lib.FA_ERR_INVALID_ARG
     assert call(pages=0) == _lib.FA_ERR_INVALID_ARG
     assert call(bt=0) == _lib.FA_ERR_INVALID_ARG          # a paged cache needs its table

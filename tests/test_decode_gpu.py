@@ -119,7 +119,7 @@ def test_kvcache_null_lengths_and_no_lse():
 
 # --- paged cache ------------------------------------------------------------
 
-@pytest.mark.parametrize("page_size", [32, 64, 256])
+@pytest.mark.parametrize("page_size", [16, 32, 64, 256])
 @pytest.mark.parametrize("d", [64, 128])
 def test_kvcache_paged(page_size, d):
     Nk = 4 * 256
@@ -135,15 +135,16 @@ def test_kvcache_paged(page_size, d):
             np.testing.assert_array_equal(lse, lc)
 
 
-def test_kvcache_paged_bad_page_index_reads_zeros():
+@pytest.mark.parametrize("page_size", [16, 32])
+def test_kvcache_paged_bad_page_index_reads_zeros(page_size):
     """A table entry outside [0, num_pages) inside a sequence reads as zeros:
     no fault, finite output (its keys score 0 and carry zero values)."""
     q, k, v, lens = _draw(1560, "bf16", 1, 4, 4, 1, 128, 64, [128])
-    kp, vp, table = build_pages(k, v, lens, 32, 1560)
+    kp, vp, table = build_pages(k, v, lens, page_size, 1560)
     table[0, 1] = 10 ** 6
     kz, vz = k.copy(), v.copy()
-    kz[:, :, 32:64] = 0
-    vz[:, :, 32:64] = 0
+    kz[:, :, page_size:2 * page_size] = 0
+    vz[:, :, page_size:2 * page_size] = 0
     qd, kd, vd = to_dev(q, "bf16"), to_dev(kp, "bf16"), to_dev(vp, "bf16")
     announce("kvcache paged bad page index")
     o, lse = fa.fwd_kvcache_paged(qd, kd, vd, torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda(),
