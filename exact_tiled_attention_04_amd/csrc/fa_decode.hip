@@ -174,12 +174,17 @@ struct Decode {
   // 16 slot + 15 (slot = 2t + half), based 16 half rows before the page so
   // that the tile's row offsets (rows 16 half .. 16 half + 15) address it,
   // and bounded to the sequence's rows of the page (offsets below 16 half
-  // rows are never used).  A slot past the sequence reads no table entry.
+  // rows are never used).
   static __device__ __forceinline__ __amdgpu_buffer_rsrc_t half_src(const DecodeParams& p, const void* base,
                                                                    int b, int hk, int L, int slot, int half) {
     const int row_bytes = p.row_stride * 2;
-    const bool live = slot * 16 < L;  // then slot < max_pages, as L <= 16 * max_pages
-    const int page = live ? scalar_load(p.block_table, (long long)b * p.max_pages + slot) : -1;
+    // the entry is read unconditionally (clamped into the table's row), so
+    // the lookups of both halves issue together; a slot past the sequence
+    // (slot * 16 >= L; below that slot < max_pages, as L <= 16 max_pages)
+    // ignores what it read
+    const bool live = slot * 16 < L;
+    const int entry = scalar_load(p.block_table, (long long)b * p.max_pages + min(slot, p.max_pages - 1));
+    const int page = live ? entry : -1;
     const bool ok = page >= 0 && page < p.num_pages;
     const int rows = min(16, L - slot * 16);
     const char* pb = (const char*)base + ((long long)(ok ? page : 0) * 16 * p.row_stride + (long long)hk * D) * 2 -
