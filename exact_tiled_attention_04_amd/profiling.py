@@ -108,12 +108,18 @@ def stats_summary(d):
 
 
 def counter_per_dispatch(d, last=None):
-    """{counter: [value per dispatch]} for the attention kernel, plus the copy kernel."""
+    """{counter: [value per dispatch]} for the attention kernel, plus the copy
+    kernel: only the calibration copy's dispatches (those with the largest
+    grid among the copies; a run may hold other, small copies, whose counts
+    would dilute the factor)."""
     rows = _csv(d, "counter_collection.csv")
+    copy_grids = [int(r.get("Grid_Size") or 0) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+    big = max(copy_grids, default=0)
     attn, copy = {}, {}
     for r in rows:
         name = r["Kernel_Name"]
-        target = attn if _is_attn(name) else copy if "copyBuffer" in name else None
+        is_cal = "copyBuffer" in name and int(r.get("Grid_Size") or 0) == big
+        target = attn if _is_attn(name) else copy if is_cal else None
         if target is None:
             continue
         key = (r["Dispatch_Id"], r["Counter_Name"])

@@ -64,3 +64,21 @@ def test_stored_traffic_files_are_well_formed():
             assert len(rec["kernel_source_sha256"]) == 64
             assert rec["hbm_bytes_per_launch"] == pytest.approx(rec["fetch_bytes"] + rec["write_bytes"], abs=2)
             assert rec["commands"] and all("rocprofv3" in c for c in rec["commands"])
+
+
+def test_calibration_uses_only_the_large_copy(tmp_path, monkeypatch):
+    """A small copy in the same counter run must not dilute the calibration
+    factor: only the copies with the largest grid count."""
+    from exact_tiled_attention_04_amd import profiling
+    rows = [("1", "__amd_rocclr_copyBuffer", "512", "3.0"),
+            ("2", "__amd_rocclr_copyBuffer", "131072", "524300.0"),
+            ("3", "void fa::(anonymous namespace)::decode_split_kernel<>", "64", "1000.0"),
+            ("4", "__amd_rocclr_copyBuffer", "131072", "524298.0")]
+    with open(tmp_path / "run_counter_collection.csv", "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Grid_Size,Counter_Name,Counter_Value\n")
+        for disp, name, grid, val in rows:
+            f.write(f'{disp},"{name}",{grid},FETCH_SIZE,{val}\n')
+    monkeypatch.setattr(profiling, "KERNEL_KEY", "decode_split")
+    attn, copy = profiling.counter_per_dispatch(str(tmp_path))
+    assert copy["FETCH_SIZE"] == [524300.0, 524298.0]
+    assert attn["FETCH_SIZE"] == [1000.0]
