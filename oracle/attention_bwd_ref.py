@@ -27,10 +27,14 @@ backward formulas: the ones above are the derivative of the forward, which is
 the plainest reading of "the gradient of exact attention".
 
 Optionally the function also returns, for error bounds in tests, the same
-products taken over absolute values (|P|^T |dO|, scale |dS| |K|,
-scale |dS|^T |Q|) and the row terms F_i = sum_c |do_ic| (P |V|)_ic -- a bound
-on sum_c |do_ic| |o_ic| that also covers a rounded P inside o -- with their
-products scale (P * F) |K| and scale (P * F)^T |Q|.
+products taken over absolute values (|P|^T |dO|, |scale| |dS| |K|,
+|scale| |dS|^T |Q|) and the row terms F_i = sum_c |do_ic| (P |V|)_ic -- a
+bound on sum_c |do_ic| |o_ic| that also covers a rounded P inside o -- with
+their products |scale| (P * F) |K| and |scale| (P * F)^T |Q|; and the same
+products with P and dS replaced by the visibility matrix (1 where key j is
+visible to query i, else 0): Vis^T |dO|, |scale| Vis |K|, |scale| Vis^T |Q|
+('dv_v', 'dq_v', 'dk_v'), the sums an absolute per-entry error of P or dS
+can reach.
 """
 from __future__ import annotations
 
@@ -62,7 +66,8 @@ def _one_kv_head(qs, kh, vh, dos, causal, window_left, scale, bounds, shift=0):
     mag = None
     if bounds:
         mag = {"dq": np.zeros((G, N, d)), "dk": np.zeros((Nk, d)), "dv": np.zeros((Nk, d)),
-               "dq_f": np.zeros((G, N, d)), "dk_f": np.zeros((Nk, d))}
+               "dq_f": np.zeros((G, N, d)), "dk_f": np.zeros((Nk, d)),
+               "dq_v": np.zeros((G, N, d)), "dk_v": np.zeros((Nk, d)), "dv_v": np.zeros((Nk, d))}
     if Nk == 0:
         return dq, dk, dv, mag
     for g in range(G):
@@ -72,7 +77,8 @@ def _one_kv_head(qs, kh, vh, dos, causal, window_left, scale, bounds, shift=0):
             pos = r + shift
             # recompute the probabilities of these rows against every key
             S = scale * (qh[r] @ kh.T)
-            S[masked(pos[:, None], keys[None, :], causal, window_left)] = -np.inf
+            hidden = masked(pos[:, None], keys[None, :], causal, window_left)
+            S[hidden] = -np.inf
             m = S.max(axis=1, keepdims=True)
             m[~np.isfinite(m)] = 0.0  # a row that sees no key: every E below is 0
             E = np.exp(S - m)
@@ -88,12 +94,16 @@ def _one_kv_head(qs, kh, vh, dos, causal, window_left, scale, bounds, shift=0):
             if bounds:
                 A = np.abs(dS)
                 mag["dv"] += P.T @ np.abs(doh[r])
-                mag["dq"][g, r] = scale * (A @ np.abs(kh))
-                mag["dk"] += scale * (A.T @ np.abs(qh[r]))
+                mag["dq"][g, r] = abs(scale) * (A @ np.abs(kh))
+                mag["dk"] += abs(scale) * (A.T @ np.abs(qh[r]))
                 F = (np.abs(doh[r]) * (P @ np.abs(vh))).sum(axis=1, keepdims=True)
                 PF = P * F
-                mag["dq_f"][g, r] = scale * (PF @ np.abs(kh))
-                mag["dk_f"] += scale * (PF.T @ np.abs(qh[r]))
+                mag["dq_f"][g, r] = abs(scale) * (PF @ np.abs(kh))
+                mag["dk_f"] += abs(scale) * (PF.T @ np.abs(qh[r]))
+                Vis = (~hidden).astype(np.float64)
+                mag["dv_v"] += Vis.T @ np.abs(doh[r])
+                mag["dq_v"][g, r] = abs(scale) * (Vis @ np.abs(kh))
+                mag["dk_v"] += abs(scale) * (Vis.T @ np.abs(qh[r]))
     return dq, dk, dv, mag
 
 
@@ -131,7 +141,8 @@ def attention_bwd(q, k, v, do, causal: bool = False, window_left: int = -1,
     mags = None
     if bounds:
         mags = {"dq": np.zeros_like(dq), "dk": np.zeros_like(dk), "dv": np.zeros_like(dv),
-                "dq_f": np.zeros_like(dq), "dk_f": np.zeros_like(dk)}
+                "dq_f": np.zeros_like(dq), "dk_f": np.zeros_like(dk),
+                "dq_v": np.zeros_like(dq), "dk_v": np.zeros_like(dk), "dv_v": np.zeros_like(dv)}
     if B * Hq * N == 0:
         return (dq, dk, dv, mags) if bounds else (dq, dk, dv)
 
@@ -145,14 +156,13 @@ def attention_bwd(q, k, v, do, causal: bool = False, window_left: int = -1,
         for gi, h in enumerate(heads):
             dq[b, h] = gq[gi]
             if bounds:
-                mags["dq"][b, h] = mag["dq"][gi]
-                mags["dq_f"][b, h] = mag["dq_f"][gi]
+                for key in ("dq", "dq_f", "dq_v"):
+                    mags[key][b, h] = mag[key][gi]
         dk[b, hk] = gk
         dv[b, hk] = gv
         if bounds:
-            mags["dk"][b, hk] = mag["dk"]
-            mags["dv"][b, hk] = mag["dv"]
-            mags["dk_f"][b, hk] = mag["dk_f"]
+            for key in ("dk", "dv", "dk_f", "dk_v", "dv_v"):
+                mags[key][b, hk] = mag[key]
 
     nthreads = threads or len(os.sched_getaffinity(0))
     nthreads = max(1, min(nthreads, B * Hkv))
@@ -201,7 +211,8 @@ def attention_bwd_varlen(q, k, v, do, cu_seqlens_q, cu_seqlens_k, causal: bool =
     mags = None
     if bounds:
         mags = {"dq": np.zeros_like(dq), "dk": np.zeros_like(dk), "dv": np.zeros_like(dv),
-                "dq_f": np.zeros_like(dq), "dk_f": np.zeros_like(dk)}
+                "dq_f": np.zeros_like(dq), "dk_f": np.zeros_like(dk),
+                "dq_v": np.zeros_like(dq), "dk_v": np.zeros_like(dk), "dv_v": np.zeros_like(dv)}
 
     def work(bk):
         b, hk = divmod(bk, Hkv)
@@ -216,12 +227,15 @@ def attention_bwd_varlen(q, k, v, do, cu_seqlens_q, cu_seqlens_k, causal: bool =
             if bounds:
                 mags["dq"][q0:q1, h] = mag["dq"][gi]
                 mags["dq_f"][q0:q1, h] = mag["dq_f"][gi]
+                mags["dq_v"][q0:q1, h] = mag["dq_v"][gi]
         dk[k0:k1, hk] = gk
         dv[k0:k1, hk] = gv
         if bounds:
             mags["dk"][k0:k1, hk] = mag["dk"]
             mags["dv"][k0:k1, hk] = mag["dv"]
             mags["dk_f"][k0:k1, hk] = mag["dk_f"]
+            mags["dk_v"][k0:k1, hk] = mag["dk_v"]
+            mags["dv_v"][k0:k1, hk] = mag["dv_v"]
 
     n = (len(cq) - 1) * Hkv
     nthreads = max(1, min(threads or len(os.sched_getaffinity(0)), max(n, 1)))

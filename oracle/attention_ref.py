@@ -73,7 +73,7 @@ def _one_head(qh, kh, vh, rows, causal, window_left, scale, tail=None):
             mag_pv[s0:s0 + len(r)] = P @ np.abs(vh)
             small = np.minimum(P, tail * P.max(axis=1, keepdims=True))
             mag_tail[s0:s0 + len(r)] = small @ np.abs(vh)
-            A = scale * (np.abs(qh[r]) @ np.abs(kh).T)
+            A = abs(scale) * (np.abs(qh[r]) @ np.abs(kh).T)
             A[masked(r[:, None], keys[None, :], causal, window_left)] = 0.0
             mag_s[s0:s0 + len(r)] = A.max(axis=1)
     if tail is not None:
@@ -95,7 +95,7 @@ def attention_fwd(q, k, v, causal: bool = False, window_left: int = -1,
     bounds, shaped like o: 'pv' = P|V| and 'tail' = sum_j min(p_ij, tail *
     max_j p_ij) |v_j| (the mass of probabilities below that fraction of their
     row's largest, as if dropped, bounded by it), shaped like o, and 'sabs' =
-    max over visible j of scale * sum_c |q_ic| |k_jc|, shaped like lse (a
+    max over visible j of |scale| * sum_c |q_ic| |k_jc|, shaped like lse (a
     bound on every visible score's size and on what its sum accumulates).
 
     Raises ValueError on inconsistent shapes, Hq not a multiple of Hkv, or

@@ -3,7 +3,7 @@
 The forward oracle's optional magnitudes (``attention_fwd(..., tail=f)``:
 'pv' = P|V|, 'tail' = sum_j min(p_ij, f max_j p_ij) |v_j|, 'sabs') and the
 gradient oracle's (``attention_bwd(..., bounds=True)``: 'dv' = P^T |dO|,
-'dq' = scale |dS| |K|, 'dk' = scale |dS|^T |Q|, 'dq_f', 'dk_f' from the row
+'dq' = |scale| |dS| |K|, 'dk' = |scale| |dS|^T |Q|, 'dq_f', 'dk_f' from the row
 terms F_i = sum_c |do_ic| (P|V|)_ic) set how wide the parity bounds of the
 backward and FP8 kernels are.  Checking only that they dominate |O| or |g|
 would let a bound that is too loose (probabilities left unnormalised, a
@@ -18,7 +18,8 @@ term is pinned to its value:
   has |dS_i0| = |dS_i1| = p_i0 p_i1 |dP_i0 - dP_i1| with p_i0 the logistic
   function of s_i0 - s_i1;
 - brute force: every term recomputed element by element with Python loops,
-  ``math.exp`` and ``math.fsum`` on tiny inputs, all mask kinds, GQA.
+  ``math.exp`` and ``math.fsum`` on tiny inputs, all mask kinds, GQA, positive,
+  negative and zero scales (the terms are magnitudes: they carry |scale|).
 
 Each pin takes the oracle callable and raises AssertionError on a mismatch;
 ``tests/test_oracle_bounds.py`` runs them on the oracle and on copies of it
@@ -74,7 +75,7 @@ def fwd_mags_brute(q, k, v, causal, wl, scale, frac):
                 for c in range(d):
                     pv[b, h, i, c] = math.fsum(p[j] * abs(vh[j, c]) for j in vis)
                     tail[b, h, i, c] = math.fsum(min(p[j], frac * pmax) * abs(vh[j, c]) for j in vis)
-                sabs[b, h, i] = max(scale * math.fsum(abs(q[b, h, i, c]) * abs(kh[j, c]) for c in range(d))
+                sabs[b, h, i] = max(abs(scale) * math.fsum(abs(q[b, h, i, c]) * abs(kh[j, c]) for c in range(d))
                                     for j in vis)
     return {"pv": pv, "tail": tail, "sabs": sabs}
 
@@ -105,24 +106,35 @@ def _group_mags(qs, kh, vh, dos, causal, wl, scale, shift=0):
     for gi in range(G):
         for i, (vis, p, dS, F) in enumerate(terms[gi]):
             for c in range(d):
-                dq[gi, i, c] = scale * math.fsum(abs(dS[j]) * abs(kh[j, c]) for j in vis)
-                dq_f[gi, i, c] = scale * math.fsum(p[j] * F * abs(kh[j, c]) for j in vis)
+                dq[gi, i, c] = abs(scale) * math.fsum(abs(dS[j]) * abs(kh[j, c]) for j in vis)
+                dq_f[gi, i, c] = abs(scale) * math.fsum(p[j] * F * abs(kh[j, c]) for j in vis)
+    dq_v = np.zeros((G, N, d))
+    for gi in range(G):
+        for i, (vis, p, dS, F) in enumerate(terms[gi]):
+            for c in range(d):
+                dq_v[gi, i, c] = abs(scale) * math.fsum(abs(kh[j, c]) for j in vis)
     dk = np.zeros((Nk, d))
     dk_f = np.zeros((Nk, d))
     dv = np.zeros((Nk, d))
+    dk_v = np.zeros((Nk, d))
+    dv_v = np.zeros((Nk, d))
     for j in range(Nk):
         for c in range(d):
-            a, bf, cv = [], [], []
+            a, bf, cv, kv, vv = [], [], [], [], []
             for gi in range(G):
                 for i, (vis, p, dS, F) in enumerate(terms[gi]):
                     if j in p:
                         a.append(abs(dS[j]) * abs(qs[gi, i, c]))
                         bf.append(p[j] * F * abs(qs[gi, i, c]))
                         cv.append(p[j] * abs(dos[gi, i, c]))
-            dk[j, c] = scale * math.fsum(a)
-            dk_f[j, c] = scale * math.fsum(bf)
+                        kv.append(abs(qs[gi, i, c]))
+                        vv.append(abs(dos[gi, i, c]))
+            dk[j, c] = abs(scale) * math.fsum(a)
+            dk_f[j, c] = abs(scale) * math.fsum(bf)
             dv[j, c] = math.fsum(cv)
-    return {"dq": dq, "dq_f": dq_f, "dk": dk, "dk_f": dk_f, "dv": dv}
+            dk_v[j, c] = abs(scale) * math.fsum(kv)
+            dv_v[j, c] = math.fsum(vv)
+    return {"dq": dq, "dq_f": dq_f, "dk": dk, "dk_f": dk_f, "dv": dv, "dq_v": dq_v, "dk_v": dk_v, "dv_v": dv_v}
 
 
 def bwd_mags_brute(q, k, v, do, causal, wl, scale):
@@ -132,13 +144,15 @@ def bwd_mags_brute(q, k, v, do, causal, wl, scale):
     Hkv = k.shape[1]
     G = Hq // Hkv
     out = {"dq": np.zeros_like(q), "dq_f": np.zeros_like(q), "dk": np.zeros_like(k), "dk_f": np.zeros_like(k),
-           "dv": np.zeros_like(v)}
+           "dv": np.zeros_like(v), "dq_v": np.zeros_like(q), "dk_v": np.zeros_like(k), "dv_v": np.zeros_like(v)}
     for b in range(B):
         for hk in range(Hkv):
             hs = slice(hk * G, (hk + 1) * G)
             m = _group_mags(q[b, hs], k[b, hk], v[b, hk], do[b, hs], causal, wl, scale)
-            out["dq"][b, hs], out["dq_f"][b, hs] = m["dq"], m["dq_f"]
-            out["dk"][b, hk], out["dk_f"][b, hk], out["dv"][b, hk] = m["dk"], m["dk_f"], m["dv"]
+            for key in ("dq", "dq_f", "dq_v"):
+                out[key][b, hs] = m[key]
+            for key in ("dk", "dk_f", "dv", "dk_v", "dv_v"):
+                out[key][b, hk] = m[key]
     return out
 
 
@@ -156,7 +170,8 @@ def _close(got, want, what, rel=1e-12):
 
 def pin_fwd_mag_brute_force(fwd_mag):
     """Every forward magnitude equals its element-by-element brute force."""
-    cases = [(1, 2, 1, 7, 3, 0.6, 2.0 ** -3), (2, 4, 2, 9, 4, 0.35, 0.5), (1, 3, 3, 5, 2, 1.3, 2.0 ** -10)]
+    cases = [(1, 2, 1, 7, 3, 0.6, 2.0 ** -3), (2, 4, 2, 9, 4, 0.35, 0.5), (1, 3, 3, 5, 2, 1.3, 2.0 ** -10),
+             (1, 2, 1, 6, 3, -0.7, 2.0 ** -2), (1, 2, 2, 5, 2, 0.0, 0.5)]
     for ci, (B, Hq, Hkv, N, d, scale, frac) in enumerate(cases):
         q, k, v = random_inputs(900 + ci, "f32", B, Hq, Hkv, N, d, mult=2.0)
         for causal, wl in MASKS:
@@ -197,14 +212,15 @@ def pin_fwd_mag_closed_forms(fwd_mag):
 def pin_bwd_mag_brute_force(bwd_mag):
     """Every gradient magnitude equals its element-by-element brute force
     (GQA groups of 1 and 2, every mask kind)."""
-    cases = [(1, 2, 1, 6, 3, 0.7), (1, 2, 2, 5, 4, 1.1), (2, 4, 2, 4, 2, 0.45)]
+    cases = [(1, 2, 1, 6, 3, 0.7), (1, 2, 2, 5, 4, 1.1), (2, 4, 2, 4, 2, 0.45), (1, 2, 1, 5, 3, -0.9),
+             (1, 4, 2, 4, 2, -0.3)]
     for ci, (B, Hq, Hkv, N, d, scale) in enumerate(cases):
         q, k, v = random_inputs(920 + ci, "f32", B, Hq, Hkv, N, d, mult=1.5)
         do = np.random.default_rng(930 + ci).standard_normal((B, Hq, N, d))
         for causal, wl in MASKS:
             m = bwd_mag(q, k, v, do, causal, wl, scale)[3]
             want = bwd_mags_brute(q, k, v, do, causal, wl, scale)
-            for key in ("dq", "dk", "dv", "dq_f", "dk_f"):
+            for key in ("dq", "dk", "dv", "dq_f", "dk_f", "dq_v", "dk_v", "dv_v"):
                 _close(m[key], want[key], f"{key} case {ci} causal={causal} wl={wl}")
 
 
@@ -241,6 +257,38 @@ def pin_bwd_mag_closed_forms(bwd_mag):
                 n = {i: sum(1 for jj in range(N) if not _hidden(i, jj, causal, wl)) for _, i in rows}
                 want = 0.6 * math.fsum(F[0, h, i] / n[i] for h, i in rows)
                 _close(m["dk_f"][0, hk, j], np.full(d, want), f"dk_f equal keys j={j} causal={causal} wl={wl}")
+
+
+def pin_bwd_mag_visibility(bwd_mag):
+    """The visibility products: with no mask every key is visible to every
+    query, so dv_v_j = sum over the group's rows of |dO| and dq_v_i =
+    |scale| sum_j |K_j| for every row; a causal mask gives key j the rows
+    i >= j and row i the keys j <= i (prefix and suffix sums); the window of
+    0 keys (with causal) leaves only the diagonal."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 9, 3
+    q, k, v = random_inputs(960, "f32", B, Hq, Hkv, N, d)
+    do = np.random.default_rng(961).standard_normal((B, Hq, N, d))
+    G = Hq // Hkv
+    aq, ak, ado = np.abs(q).astype(np.float64), np.abs(k).astype(np.float64), np.abs(do)
+    for scale in (0.7, -0.4):
+        m = bwd_mag(q, k, v, do, False, -1, scale)[3]
+        for hk in range(Hkv):
+            grp = slice(hk * G, (hk + 1) * G)
+            _close(m["dv_v"][0, hk], np.broadcast_to(ado[0, grp].sum(axis=(0, 1)), (N, d)), "dv_v no mask")
+            _close(m["dk_v"][0, hk], np.broadcast_to(abs(scale) * aq[0, grp].sum(axis=(0, 1)), (N, d)), "dk_v no mask")
+            for h in range(hk * G, (hk + 1) * G):
+                _close(m["dq_v"][0, h], np.broadcast_to(abs(scale) * ak[0, hk].sum(axis=0), (N, d)), "dq_v no mask")
+        m = bwd_mag(q, k, v, do, True, -1, scale)[3]
+        for hk in range(Hkv):
+            grp = slice(hk * G, (hk + 1) * G)
+            suffix = np.cumsum(ado[0, grp].sum(axis=0)[::-1], axis=0)[::-1]
+            _close(m["dv_v"][0, hk], suffix, "dv_v causal")
+            for h in range(hk * G, (hk + 1) * G):
+                _close(m["dq_v"][0, h], abs(scale) * np.cumsum(ak[0, hk], axis=0), "dq_v causal")
+        m = bwd_mag(q, k, v, do, True, 0, scale)[3]
+        for hk in range(Hkv):
+            _close(m["dv_v"][0, hk], ado[0, hk * G:(hk + 1) * G].sum(axis=0), "dv_v diagonal")
+            _close(m["dk_v"][0, hk], abs(scale) * aq[0, hk * G:(hk + 1) * G].sum(axis=0), "dk_v diagonal")
 
 
 def pin_bwd_mag_two_keys(bwd_mag):
@@ -297,12 +345,12 @@ def pin_varlen_bwd_mag_brute_force(bwd_varlen_mag):
                 hs = slice(hk * (Hq // Hkv), (hk + 1) * (Hq // Hkv))
                 want = _group_mags(q[a:z, hs].transpose(1, 0, 2), k[ka:kz, hk], v[ka:kz, hk],
                                    do[a:z, hs].transpose(1, 0, 2), causal, wl, 0.8, shift=lk - lq)
-                for key in ("dq", "dq_f"):
+                for key in ("dq", "dq_f", "dq_v"):
                     _close(m[key][a:z, hs].transpose(1, 0, 2), want[key], f"{key} sequence {b} c={causal} wl={wl}")
-                for key in ("dk", "dk_f", "dv"):
+                for key in ("dk", "dk_f", "dv", "dk_v", "dv_v"):
                     _close(m[key][ka:kz, hk], want[key], f"{key} sequence {b} c={causal} wl={wl}")
 
 
 FWD_MAG_PINS = [pin_fwd_mag_brute_force, pin_fwd_mag_closed_forms]
-BWD_MAG_PINS = [pin_bwd_mag_brute_force, pin_bwd_mag_closed_forms, pin_bwd_mag_two_keys]
+BWD_MAG_PINS = [pin_bwd_mag_brute_force, pin_bwd_mag_closed_forms, pin_bwd_mag_visibility, pin_bwd_mag_two_keys]
 VARLEN_BWD_MAG_PINS = [pin_varlen_bwd_mag_brute_force]

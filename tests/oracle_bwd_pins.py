@@ -180,7 +180,47 @@ def pin_bwd_key_permutation(bwd):
     np.testing.assert_allclose(dv2, dv[:, :, perm], rtol=0, atol=1e-12)
 
 
-ALL_BWD_PINS = [pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_equal_keys, pin_bwd_single_key,
+def pin_bwd_zero_and_negative_scale(bwd):
+    """scale = 0: P is uniform over the visible keys whatever Q and K are, so
+    dQ = dK = 0 and dV_j = sum over the group and the rows i that see j of
+    dO_i / n_i.  scale < 0: central finite differences of the forward oracle."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 7, 3
+    q, k, v = (x.astype(np.float64) for x in random_inputs(750, "f32", B, Hq, Hkv, N, d))
+    do = _rand_do(751, B, Hq, N, d)
+    G = Hq // Hkv
+    for causal, wl in MASKS:
+        dq, dk, dv = bwd(q, k, v, do, causal, wl, 0.0)
+        np.testing.assert_allclose(dq, 0.0, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dk, 0.0, rtol=0, atol=1e-13)
+        vis = _visible(N, causal, wl).astype(np.float64)
+        W = vis / vis.sum(axis=1, keepdims=True)
+        for hk in range(Hkv):
+            want = sum(W.T @ do[0, hk * G + g] for g in range(G))
+            np.testing.assert_allclose(dv[0, hk], want, rtol=0, atol=1e-12)
+    h = 1e-5
+    for causal, wl in [(False, -1), (True, 2)]:
+        scale = -0.8
+
+        def loss(qq, kk, vv):
+            o, _ = attention_fwd(qq, kk, vv, causal, wl, scale, threads=1)
+            return float((o * do).sum())
+        grads = bwd(q, k, v, do, causal, wl, scale)
+        for name, x, g in zip("qkv", (q, k, v), grads):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                args_p = {"q": q, "k": k, "v": v}
+                args_m = dict(args_p)
+                xp = x.copy()
+                xp[idx] += h
+                xm = x.copy()
+                xm[idx] -= h
+                args_p[name], args_m[name] = xp, xm
+                num[idx] = (loss(args_p["q"], args_p["k"], args_p["v"]) -
+                            loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * h)
+            np.testing.assert_allclose(g, num, rtol=0, atol=2e-8, err_msg=f"d{name} scale={scale} causal={causal}")
+
+
+ALL_BWD_PINS = [pin_bwd_finite_differences, pin_bwd_zero_and_negative_scale, pin_bwd_torch_autograd, pin_bwd_equal_keys, pin_bwd_single_key,
                 pin_bwd_sum_rules, pin_bwd_linearity, pin_bwd_key_permutation]
 
 

@@ -196,5 +196,36 @@ def pin_key_permutation(fwd):
     np.testing.assert_allclose(l1, l0, rtol=0, atol=1e-12)
 
 
+def pin_zero_and_negative_scale(fwd):
+    """scale = 0: every visible score is 0, so O_i is the mean of the visible
+    V rows and lse_i = ln(n_i).  scale < 0: torch's float64 attention agrees,
+    and the keys the query is least aligned with weigh most (with q_i = k_j*
+    for one key j*, that key gets the smallest probability)."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 15, 6
+    q, k, v = random_inputs(18, "f32", B, Hq, Hkv, N, d)
+    for causal, wl in MASKS:
+        o, lse = fwd(q, k, v, causal, wl, 0.0)
+        vis = _visible(N, causal, wl)
+        for h in range(Hq):
+            for i in range(N):
+                np.testing.assert_allclose(o[0, h, i], v[0, h // 2, vis[i]].astype(np.float64).mean(axis=0),
+                                           rtol=0, atol=1e-12)
+                assert abs(lse[0, h, i] - math.log(len(vis[i]))) <= 1e-12
+        for scale in (-0.6, -1.0 / math.sqrt(d)):
+            o, lse = fwd(q, k, v, causal, wl, scale)
+            ro, rl = _torch_reference(q, k, v, causal, wl, scale)
+            np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12, err_msg=f"o scale={scale} causal={causal} wl={wl}")
+            np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-12, err_msg=f"lse scale={scale}")
+    # V = identity exposes P: under a negative scale the aligned key is the
+    # least likely one of the row
+    kk = np.random.default_rng(19).standard_normal((1, 1, 6, 6))
+    qq = np.repeat(kk[:, :, 2:3], 6, axis=2) * 3.0
+    P, _ = fwd(qq, kk, np.eye(6)[None, None], False, -1, -0.5)
+    assert (P[0, 0].argmin(axis=-1) == 2).all()
+    P, _ = fwd(qq, kk, np.eye(6)[None, None], False, -1, 0.5)
+    assert (P[0, 0].argmax(axis=-1) == 2).all()
+
+
 ALL_PINS = [pin_hand_worked, pin_torch_sdpa, pin_rows_are_probabilities, pin_shift_invariance,
+            pin_zero_and_negative_scale,
             pin_all_equal_keys, pin_one_hot_dominant, pin_special_cases, pin_key_permutation]

@@ -74,9 +74,11 @@ FWD_MAG_MUTANTS = [
      "np.minimum(P, tail * P.max(axis=1, keepdims=True))", "np.minimum(P, tail * P.max(axis=0, keepdims=True))"),
     ("tail weighted by |K| instead of |V|", "mag_tail[s0:s0 + len(r)] = small @ np.abs(vh)",
      "mag_tail[s0:s0 + len(r)] = small @ np.abs(kh)"),
-    ("score magnitude without |Q|", "A = scale * (np.abs(qh[r]) @ np.abs(kh).T)", "A = scale * (qh[r] @ np.abs(kh).T)"),
-    ("score magnitude without the scale", "A = scale * (np.abs(qh[r]) @ np.abs(kh).T)",
+    ("score magnitude without |Q|", "A = abs(scale) * (np.abs(qh[r]) @ np.abs(kh).T)", "A = abs(scale) * (qh[r] @ np.abs(kh).T)"),
+    ("score magnitude without the scale", "A = abs(scale) * (np.abs(qh[r]) @ np.abs(kh).T)",
      "A = (np.abs(qh[r]) @ np.abs(kh).T)"),
+    ("score magnitude with the signed scale", "A = abs(scale) * (np.abs(qh[r]) @ np.abs(kh).T)",
+     "A = scale * (np.abs(qh[r]) @ np.abs(kh).T)"),
     ("score magnitude over masked keys too", "            A[masked(r[:, None], keys[None, :], causal, window_left)] = 0.0\n",
      ""),
 ]
@@ -90,18 +92,22 @@ def test_fwd_magnitude_pins_catch_planted_mistake(name, old, new):
 
 
 BWD_MAG_MUTANTS = [
-    ("dq without the scale", 'mag["dq"][g, r] = scale * (A @ np.abs(kh))', 'mag["dq"][g, r] = (A @ np.abs(kh))'),
-    ("dq with the scale twice", 'mag["dq"][g, r] = scale * (A @ np.abs(kh))',
+    ("dq without the scale", 'mag["dq"][g, r] = abs(scale) * (A @ np.abs(kh))', 'mag["dq"][g, r] = (A @ np.abs(kh))'),
+    ("dq with the scale twice", 'mag["dq"][g, r] = abs(scale) * (A @ np.abs(kh))',
      'mag["dq"][g, r] = scale * scale * (A @ np.abs(kh))'),
-    ("dq through |Q| instead of |K|", 'mag["dq"][g, r] = scale * (A @ np.abs(kh))',
+    ("dq through |Q| instead of |K|", 'mag["dq"][g, r] = abs(scale) * (A @ np.abs(kh))',
      'mag["dq"][g, r] = scale * (A @ np.abs(qh[r]))'),
-    ("dq through |V| instead of |K|", 'mag["dq"][g, r] = scale * (A @ np.abs(kh))',
+    ("dq through |V| instead of |K|", 'mag["dq"][g, r] = abs(scale) * (A @ np.abs(kh))',
      'mag["dq"][g, r] = scale * (A @ np.abs(vh))'),
-    ("dk through |K| instead of |Q|", 'mag["dk"] += scale * (A.T @ np.abs(qh[r]))',
-     'mag["dk"] += scale * (A.T @ np.abs(kh))'),
-    ("dk without the scale", 'mag["dk"] += scale * (A.T @ np.abs(qh[r]))', 'mag["dk"] += (A.T @ np.abs(qh[r]))'),
-    ("dk not summed over the group", 'mag["dk"] += scale * (A.T @ np.abs(qh[r]))',
-     'mag["dk"] = scale * (A.T @ np.abs(qh[r]))'),
+    ("dq with the signed scale", 'mag["dq"][g, r] = abs(scale) * (A @ np.abs(kh))',
+     'mag["dq"][g, r] = scale * (A @ np.abs(kh))'),
+    ("dk through |K| instead of |Q|", 'mag["dk"] += abs(scale) * (A.T @ np.abs(qh[r]))',
+     'mag["dk"] += abs(scale) * (A.T @ np.abs(kh))'),
+    ("dk without the scale", 'mag["dk"] += abs(scale) * (A.T @ np.abs(qh[r]))', 'mag["dk"] += (A.T @ np.abs(qh[r]))'),
+    ("dk with the signed scale", 'mag["dk"] += abs(scale) * (A.T @ np.abs(qh[r]))',
+     'mag["dk"] += scale * (A.T @ np.abs(qh[r]))'),
+    ("dk not summed over the group", 'mag["dk"] += abs(scale) * (A.T @ np.abs(qh[r]))',
+     'mag["dk"] = abs(scale) * (A.T @ np.abs(qh[r]))'),
     ("|dS| replaced by dS", "A = np.abs(dS)", "A = dS"),
     ("|dS| replaced by |dP|", "A = np.abs(dS)", "A = np.abs(dP)"),
     ("dv from the unnormalised exponentials", 'mag["dv"] += P.T @ np.abs(doh[r])', 'mag["dv"] += E.T @ np.abs(doh[r])'),
@@ -109,11 +115,21 @@ BWD_MAG_MUTANTS = [
     ("row term without |dO|", "F = (np.abs(doh[r]) * (P @ np.abs(vh)))", "F = (doh[r] * (P @ np.abs(vh)))"),
     ("row term from O instead of P|V|", "F = (np.abs(doh[r]) * (P @ np.abs(vh)))", "F = (np.abs(doh[r]) * (P @ vh))"),
     ("dq_f without P", "PF = P * F", "PF = F + 0 * P"),
-    ("dq_f without the scale", 'mag["dq_f"][g, r] = scale * (PF @ np.abs(kh))', 'mag["dq_f"][g, r] = (PF @ np.abs(kh))'),
-    ("dk_f through |K| instead of |Q|", 'mag["dk_f"] += scale * (PF.T @ np.abs(qh[r]))',
-     'mag["dk_f"] += scale * (PF.T @ np.abs(kh))'),
-    ("dk_f not summed over the group", 'mag["dk_f"] += scale * (PF.T @ np.abs(qh[r]))',
-     'mag["dk_f"] = scale * (PF.T @ np.abs(qh[r]))'),
+    ("dq_f without the scale", 'mag["dq_f"][g, r] = abs(scale) * (PF @ np.abs(kh))',
+     'mag["dq_f"][g, r] = (PF @ np.abs(kh))'),
+    ("dq_f with the signed scale", 'mag["dq_f"][g, r] = abs(scale) * (PF @ np.abs(kh))',
+     'mag["dq_f"][g, r] = scale * (PF @ np.abs(kh))'),
+    ("dk_f through |K| instead of |Q|", 'mag["dk_f"] += abs(scale) * (PF.T @ np.abs(qh[r]))',
+     'mag["dk_f"] += abs(scale) * (PF.T @ np.abs(kh))'),
+    ("visibility from the masked set", "Vis = (~hidden).astype(np.float64)", "Vis = hidden.astype(np.float64)"),
+    ("visibility weighted by P", "Vis = (~hidden).astype(np.float64)", "Vis = (~hidden) * P"),
+    ("dv_v through |Q|", 'mag["dv_v"] += Vis.T @ np.abs(doh[r])', 'mag["dv_v"] += Vis.T @ np.abs(qh[r])'),
+    ("dq_v without the scale", 'mag["dq_v"][g, r] = abs(scale) * (Vis @ np.abs(kh))',
+     'mag["dq_v"][g, r] = (Vis @ np.abs(kh))'),
+    ("dk_v not summed over the group", 'mag["dk_v"] += abs(scale) * (Vis.T @ np.abs(qh[r]))',
+     'mag["dk_v"] = abs(scale) * (Vis.T @ np.abs(qh[r]))'),
+    ("dk_f not summed over the group", 'mag["dk_f"] += abs(scale) * (PF.T @ np.abs(qh[r]))',
+     'mag["dk_f"] = abs(scale) * (PF.T @ np.abs(qh[r]))'),
 ]
 
 

@@ -85,8 +85,7 @@ BWD_MUTANTS = [
     ("dV through Q", "dv += P.T @ doh[r]", "dv += P.T @ qh[r]"),
     ("dV from scores, not probabilities", "dv += P.T @ doh[r]", "dv += E.T @ doh[r]"),
     ("group sum dropped for dK", "dk += scale * (dS.T @ qh[r])", "dk = scale * (dS.T @ qh[r])"),
-    ("mask ignored in the backward", "S[masked(pos[:, None], keys[None, :], causal, window_left)] = -np.inf",
-     "S[masked(pos[:, None], keys[None, :], causal, window_left)] = S[masked(pos[:, None], keys[None, :], causal, window_left)]"),
+    ("mask ignored in the backward", "S[hidden] = -np.inf", "S[hidden] = S[hidden]"),
     ("scores without the scale", "S = scale * (qh[r] @ kh.T)", "S = (qh[r] @ kh.T)"),
 ]
 
