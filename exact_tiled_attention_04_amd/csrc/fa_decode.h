@@ -33,7 +33,8 @@ struct DecodeParams {
   int n_row_items;          // ceil(n_row_blocks / rb_per_item)
   int total_items;          // B * Hkv * n_row_items * n_splits (one wavefront each)
   int page_size, max_pages, num_pages;
-  float scale_log2;
+  float scale_log2;         // |scale| * log2(e) (log2(e) for a zero scale)
+  int q_sign;               // sign of the scale, applied to the query registers (as FwdParams)
 };
 
 hipError_t launch_decode(const DecodeParams& p, int d, bool f16, hipStream_t stream);

@@ -333,7 +333,7 @@ __global__ void __launch_bounds__(kWaves * kWaveSize) decode_split_kernel(Decode
       const unsigned short* qrow = (const unsigned short*)p.q + out_row[j] * D;
 #pragma unroll
       for (int kc = 0; kc < S::kSteps; ++kc)
-        qf[j][kc] = valid[j] ? *(const u32x4*)(qrow + 16 * kc + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
+        qf[j][kc] = valid[j] ? q_signed16(*(const u32x4*)(qrow + 16 * kc + 8 * hh), p.q_sign) : u32x4{0u, 0u, 0u, 0u};
     }
 
     // per-lane copy offsets: lane fills LDS bytes 16 lane .. +15 of each 1-KiB

@@ -61,9 +61,15 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p) {
 
   // lane r holds dims 16u + 4r .. 16u + 4r + 3 for u < kVec
   float4 qv[kVec], ov[kVec];
+  const float qsgn = (float)p.q_sign;
 #pragma unroll
   for (int u = 0; u < kVec; ++u) {
     qv[u] = myq < N ? qg[(long long)myq * kRow4 + 4 * u + r] : make_float4(0.f, 0.f, 0.f, 0.f);
+    // the scale's sign on the query (the multiplier c below is positive)
+    qv[u].x *= qsgn;
+    qv[u].y *= qsgn;
+    qv[u].z *= qsgn;
+    qv[u].w *= qsgn;
     ov[u] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float m_run = -INFINITY, l_run = 0.f;

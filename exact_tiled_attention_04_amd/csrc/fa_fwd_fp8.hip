@@ -433,7 +433,7 @@ __global__ void __launch_bounds__(kThreads, FA8_WAVES_PER_SIMD) fwd_fp8_kernel(F
   for (int kc = 0; kc < S::kSteps; ++kc) {
     if (myq < N) {
       const unsigned char* src = qg + (long long)myq * D + 64 * kc + 32 * x.hh;
-      st.qf[kc] = join(*(const u32x4*)src, *(const u32x4*)(src + 16));
+      st.qf[kc] = join(q_signed8(*(const u32x4*)src, p.q_sign), q_signed8(*(const u32x4*)(src + 16), p.q_sign));
     } else {
       st.qf[kc] = i32x8{};
     }
@@ -498,8 +498,9 @@ __global__ void __launch_bounds__(kThreads, FA8_WAVES_PER_SIMD) fwd_fp8_kernel(F
 
 template <int D>
 hipError_t launch(const FwdArgs& a, float q_scale, float k_scale, float v_scale, hipStream_t stream) {
-  FwdParams p = make_params(a, kBR);
-  p.scale_log2 = (float)((double)a.scale * q_scale * k_scale * 1.4426950408889634);
+  FwdParams p = make_params(a, kBR);  // q_sign from the sign of the scale (the Q and K scales are > 0)
+  const double c = (double)a.scale * q_scale * k_scale;
+  p.scale_log2 = (float)((c != 0.0 ? (c < 0.0 ? -c : c) : 1.0) * 1.4426950408889634);
   p.o_mult = v_scale;
   hipLaunchKernelGGL((fwd_fp8_kernel<D>), dim3(p.total_items), dim3(kThreads), 0, stream, p);
   return hipGetLastError();

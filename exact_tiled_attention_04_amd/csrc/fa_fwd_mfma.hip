@@ -525,7 +525,7 @@ __global__ void __launch_bounds__(kThreads, kWavesPerSimd) fwd_mfma_kernel(FwdPa
 #pragma unroll
   for (int kc = 0; kc < S::kSteps; ++kc) {
     if (myq < Nq)
-      st.qf[kc] = *(const u32x4*)(qg + (long long)myq * q_stride + 16 * kc + 8 * x.hh);
+      st.qf[kc] = q_signed16(*(const u32x4*)(qg + (long long)myq * q_stride + 16 * kc + 8 * x.hh), p.q_sign);
     else
       st.qf[kc] = u32x4{0u, 0u, 0u, 0u};
   }

@@ -16,7 +16,7 @@ struct FwdArgs {
   int B, Hq, Hkv, N, d;
   int causal;
   int window_left;  // -1 = no window
-  float scale;      // > 0
+  float scale;      // any finite value
   // packed sequences of different lengths (null: one N for all): q [total_q]
   // [Hq][d], k, v [total_k][Hkv][d], sequence b owning rows cu_q[b] ..
   // cu_q[b+1]-1 and keys cu_k[b] .. cu_k[b+1]-1; N is then the longest query
@@ -39,8 +39,11 @@ struct FwdParams {
   int window_left;
   int n_qblocks;     // ceil(N / rows per workgroup)
   int total_items;   // B * Hq * n_qblocks
-  float scale_log2;  // scale * log2(e): scores go straight into exp2
-                     // (FP8: times the Q and K scales)
+  float scale_log2;  // |scale| * log2(e) (1 * log2(e) for a zero scale): scores
+                     // go straight into exp2 (FP8: times the Q and K scales)
+  int q_sign;        // sign of the scale: +1; -1 (queries negated in registers,
+                     // so the positive multiplier above gives the same scores);
+                     // 0 (queries read as zeros: every visible score is 0)
   float o_mult;      // multiplier on the output: the V scale of FP8 inputs, else 1
   const int* cu_q;   // packed variable-length sequences (null: fixed N), as FwdArgs
   const int* cu_k;
@@ -87,6 +90,17 @@ __device__ __forceinline__ WorkItem decode_work_item(const FwdParams& p, int id)
   return it;
 }
 
+// The kernels take each row's maximum over the raw products q.k and multiply
+// by the scale afterwards, which is only right for a positive multiplier.
+// scale * q.k equals |scale| * (-q).k for a negative scale (negating a query
+// flips sign bits: exact), and 0 * q.k equals any positive multiple of 0.k,
+// so the kernels get a positive multiplier and the sign to apply to Q.
+template <typename P>
+inline void set_score_scale(P& p, float scale) {
+  p.q_sign = scale > 0.f ? 1 : (scale < 0.f ? -1 : 0);
+  p.scale_log2 = (scale != 0.f ? __builtin_fabsf(scale) : 1.f) * 1.4426950408889634f;
+}
+
 inline FwdParams make_params(const FwdArgs& a, int rows_per_wg) {
   FwdParams p;
   p.q = a.q;
@@ -106,7 +120,7 @@ inline FwdParams make_params(const FwdArgs& a, int rows_per_wg) {
   p.window_left = (a.window_left >= span - 1) ? -1 : a.window_left;
   p.n_qblocks = (a.N + rows_per_wg - 1) / rows_per_wg;
   p.total_items = a.B * a.Hq * p.n_qblocks;
-  p.scale_log2 = a.scale * 1.4426950408889634f;
+  set_score_scale(p, a.scale);
   p.o_mult = 1.f;
   p.cu_q = a.cu_q;
   p.cu_k = a.cu_k;
@@ -198,6 +212,8 @@ inline BwdParams make_bwd_params(const BwdArgs& a, int rows_per_wg) {
   p.items_dq = a.B * a.Hq * p.n_blocks;
   p.items_dkv = a.B * a.Hkv * p.n_kblocks;
   p.scale = a.scale;
+  // any sign: the backward masks after the exponent, and rebuilds P from the
+  // scaled score and the saved logsumexp (no row maximum is taken)
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.cu_q = a.cu_q;
   p.cu_k = a.cu_k;

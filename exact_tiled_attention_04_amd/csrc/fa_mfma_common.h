@@ -60,5 +60,19 @@ __device__ __forceinline__ s16x4 lds_read_tr(const unsigned short* base, int off
 
 constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 
+// Query registers under the sign of the scale (q_sign of the kernel
+// parameters): +1 unchanged, -1 every element negated (sign bits flipped),
+// 0 zeros.  For eight 16-bit elements and for sixteen E4M3 bytes per u32x4.
+__device__ __forceinline__ u32x4 q_signed16(u32x4 x, int sign) {
+  const unsigned keep = sign != 0 ? 0xffffffffu : 0u;
+  const unsigned flip = sign < 0 ? 0x80008000u : 0u;
+  return u32x4{(x[0] & keep) ^ flip, (x[1] & keep) ^ flip, (x[2] & keep) ^ flip, (x[3] & keep) ^ flip};
+}
+__device__ __forceinline__ u32x4 q_signed8(u32x4 x, int sign) {
+  const unsigned keep = sign != 0 ? 0xffffffffu : 0u;
+  const unsigned flip = sign < 0 ? 0x80808080u : 0u;
+  return u32x4{(x[0] & keep) ^ flip, (x[1] & keep) ^ flip, (x[2] & keep) ^ flip, (x[3] & keep) ^ flip};
+}
+
 }  // namespace mfma
 }  // namespace fa

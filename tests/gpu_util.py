@@ -64,6 +64,48 @@ def compare(o, lse, o_ref, lse_ref, dtype, label="", scaled=False):
     return max_e, mean_e, lmax
 
 
+# unit roundoff of the probabilities fed to the P V product (the 16-bit
+# kernels round P to the input type; the fp32 kernel keeps it in fp32) and
+# of the stored output
+UNIT_P = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 0.0}
+UNIT_OUT = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -24}
+SUBNORMAL_ABS = {"bf16": 0.0, "f16": 2.0 ** -25, "f32": 0.0}
+
+
+def check_rounding_bound(o, lse, q, k, v, causal, wl, scale, dtype, label=""):
+    """Every element of (o, lse) under a bound derived from the forward
+    kernels' arithmetic, against the fp64 oracle's magnitudes:
+
+        |dO| <= (u_P + (N + 8) 2^-24 + 2^-20 + 2 d 2^-24 S) P|V| + u_out |O|
+                + s (N max|V| + 1) + 2^-100 max|O|
+        |dlse| <= d 2^-24 S + (N + 8) 2^-24 + 2^-20 (16 + |lse|)
+
+    u_P: rounding of P before the P V product; N 2^-24: fp32 accumulation
+    over up to N keys; 2^-20: the exp2 and scale approximations; S = max
+    over visible keys of |scale| sum_c |q_c k_c| (``sabs``), so d 2^-24 S
+    bounds each score's fp32 error and 2 d 2^-24 S the relative change of a
+    probability it causes; u_out: rounding of the stored output; s: the
+    absolute rounding error of a probability below the type's normal range
+    (fp16: 2^-25; the kernels round unnormalised probabilities whose row
+    maximum is at least 1, so after the division by the row sum it stays at
+    most s per key) and of a stored output below that range.  The floor
+    covers probabilities below fp32's range."""
+    from oracle import attention_fwd
+    ro, rl, mag = attention_fwd(q, k, v, causal, wl, scale, tail=0.0)
+    N, d = k.shape[2], q.shape[3]
+    s = mag["sabs"][..., None]
+    bound = ((UNIT_P[dtype] + (N + 8) * 2.0 ** -24 + 2.0 ** -20 + 2 * d * 2.0 ** -24 * s) * mag["pv"]
+             + UNIT_OUT[dtype] * np.abs(ro) + SUBNORMAL_ABS[dtype] * (N * float(np.abs(v).max(initial=0)) + 1.0)
+             + 2.0 ** -100 * float(np.abs(ro).max(initial=0)))
+    lbound = d * 2.0 ** -24 * mag["sabs"] + (N + 8) * 2.0 ** -24 + 2.0 ** -20 * (16 + np.abs(rl))
+    err, lerr = np.abs(o - ro), np.abs(lse - rl)
+    worst = float((err / np.maximum(bound, 1e-300)).max(initial=0))
+    lworst = float((lerr / lbound).max(initial=0))
+    print(f"[bound] {label} dtype={dtype} worst err/bound O {worst:.3f} lse {lworst:.3f}", file=sys.stderr, flush=True)
+    assert (err <= bound).all(), f"{label}: O exceeds the rounding bound (worst ratio {worst:.3f})"
+    assert (lerr <= lbound).all(), f"{label}: lse exceeds the rounding bound (worst ratio {lworst:.3f})"
+
+
 def sample_rows(N: int, rng: np.random.Generator, n_random: int = 48, block: int = 128):
     """First and last rows, rows around query-block and key-tile edges, random rows."""
     rows = {0, 1, N - 1, N - 2}
