@@ -11,7 +11,9 @@ import ctypes
 import os
 import threading
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+# FA_LIB_PATH names another build of the same library (the host-sanitizer
+# build the CPU tests run the C-ABI checks against); by default the in-tree one.
+LIB_PATH = os.environ.get("FA_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_DTYPE_F32, FA_DTYPE_F16, FA_DTYPE_BF16 = 0, 1, 2
 DTYPE_CODES = {"f32": FA_DTYPE_F32, "f16": FA_DTYPE_F16, "bf16": FA_DTYPE_BF16}

@@ -25,8 +25,12 @@ SOURCES = ["fa_api.cpp", "fa_fwd_mfma.hip", "fa_fwd_f32.hip", "fa_bwd_mfma.hip",
 
 # Packed fp32 VALU instructions are kept out of every device code object.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-fno-honor-nans", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
           "-I", INCLUDE, "-I", CSRC]
+# Device code may assume no NaN reaches its arithmetic (inputs are finite by
+# contract); the host code's argument checks must see NaN as NaN, so it is
+# compiled without this flag.
+KERNEL_ONLY = ["-fno-honor-nans"]
 
 
 def hipcc() -> str:
@@ -36,17 +40,32 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libfa.so)")
 
 
-def build(verbose: bool = False) -> str:
+# Host-side sanitizers for the checking build: AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host code only (each flag behind
+# -Xarch_host, so device code objects are built exactly as in the product).
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile every source and link libfa.so in the package directory; with
+    ``sanitize``, the same library with host-side sanitizers into
+    ``_build/sanitize/libfa.so`` (loaded only by the sanitizer test, with the
+    sanitizer runtime preloaded)."""
     cc = hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    build_dir = os.path.join(BUILD_DIR, "sanitize") if sanitize else BUILD_DIR
+    lib_path = os.path.join(build_dir, "libfa.so") if sanitize else LIB_PATH
+    san = SANITIZE_HOST if sanitize else []
+    os.makedirs(build_dir, exist_ok=True)
     t0 = time.time()
     procs = []
     objs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc, *COMMON, *DEVICE_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        extra = KERNEL_ONLY if src.endswith(".hip") else []
+        cmd = [cc, *COMMON, *extra, *san, *DEVICE_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -61,18 +80,18 @@ def build(verbose: bool = False) -> str:
     if failed:
         msg = "\n".join(f"--- {s} ---\n{o}" for s, o in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    tmp = lib_path + f".tmp{os.getpid()}"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *san, "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB_PATH} in {time.time() - t0:.1f}s", flush=True)
-    return LIB_PATH
+        print(f"built {lib_path} in {time.time() - t0:.1f}s", flush=True)
+    return lib_path
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
+    build(verbose="-v" in sys.argv, sanitize="--sanitize-host" in sys.argv)

@@ -29,7 +29,7 @@ int fail(int status, const char* fmt, ...) {
 
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
-size_t elem_size(fa_dtype_t dt) { return dt == FA_DTYPE_F32 ? 4 : 2; }
+size_t elem_size(int dt) { return dt == FA_DTYPE_F32 ? 4 : 2; }
 
 bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -38,7 +38,7 @@ bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
 
 // Checks shared by the forward and the backward.  Returns FA_OK with
 // *empty = true when there is nothing to compute.
-int check_sizes(int B, int Hq, int Hkv, int N, int d, int window_left, float scale, fa_dtype_t dtype,
+int check_sizes(int B, int Hq, int Hkv, int N, int d, int window_left, float scale, int dtype,
                 bool* empty) {
   *empty = false;
   if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
@@ -55,15 +55,13 @@ int check_sizes(int B, int Hq, int Hkv, int N, int d, int window_left, float sca
     return fail(FA_ERR_INVALID_ARG, "window_left=%d (must be -1 or >= 0)", window_left);
   if (!std::isfinite(scale))
     return fail(FA_ERR_INVALID_ARG, "scale is not finite");
-  if (!(scale > 0.f))
-    return fail(FA_ERR_UNSUPPORTED, "scale=%g: only positive scales are supported", (double)scale);
   if (d != 64 && d != 128)
     return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d (supported: 64, 128)", d);
   return FA_OK;
 }
 
 int run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-        int N, int d, int causal, int window_left, float scale, void* stream, fa_dtype_t dtype) {
+        int N, int d, int causal, int window_left, float scale, void* stream, int dtype) {
   g_last_error[0] = '\0';
   bool empty;
   if (int st = check_sizes(B, Hq, Hkv, N, d, window_left, scale, dtype, &empty)) return st;
@@ -123,7 +121,7 @@ int run(const void* q, const void* k, const void* v, void* o, float* lse, int B,
 
 int run_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_q, const int* cu_k,
                int B, int Hq, int Hkv, int total_q, int total_k, int max_q, int max_k, int d, int causal,
-               int window_left, float scale, void* stream, fa_dtype_t dtype) {
+               int window_left, float scale, void* stream, int dtype) {
   g_last_error[0] = '\0';
   if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
     return fail(FA_ERR_UNSUPPORTED, "packed sequences support bf16 and fp16 only (dtype %d)", static_cast<int>(dtype));
@@ -135,7 +133,6 @@ int run_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
     return fail(FA_ERR_INVALID_ARG, "Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
   if (window_left < -1) return fail(FA_ERR_INVALID_ARG, "window_left=%d (must be -1 or >= 0)", window_left);
   if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale is not finite");
-  if (!(scale > 0.f)) return fail(FA_ERR_UNSUPPORTED, "scale=%g: only positive scales are supported", (double)scale);
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d (supported: 64, 128)", d);
   if (!q || !k || !v || !o || !cu_q || !cu_k)
     return fail(FA_ERR_INVALID_ARG, "null q/k/v/o/cu_seqlens pointer");
@@ -188,7 +185,7 @@ uint64_t bwd_workspace_bytes(int B, int Hq, int N);
 int run_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                    void* dq, void* dk, void* dv, float* work, const int* cu_q, const int* cu_k, int B, int Hq,
                    int Hkv, int total_q, int total_k, int max_q, int max_k, int d, int causal, int window_left,
-                   float scale, void* stream, fa_dtype_t dtype) {
+                   float scale, void* stream, int dtype) {
   g_last_error[0] = '\0';
   if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
     return fail(FA_ERR_UNSUPPORTED, "the backward supports bf16 and fp16 only (dtype %d)", static_cast<int>(dtype));
@@ -200,7 +197,6 @@ int run_bwd_varlen(const void* q, const void* k, const void* v, const void* o, c
     return fail(FA_ERR_INVALID_ARG, "Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
   if (window_left < -1) return fail(FA_ERR_INVALID_ARG, "window_left=%d (must be -1 or >= 0)", window_left);
   if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale is not finite");
-  if (!(scale > 0.f)) return fail(FA_ERR_UNSUPPORTED, "scale=%g: only positive scales are supported", (double)scale);
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d (supported: 64, 128)", d);
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !work || !cu_q || !cu_k)
     return fail(FA_ERR_INVALID_ARG, "null pointer among q/k/v/o/lse/dout/dq/dk/dv/workspace/cu_seqlens");
@@ -278,7 +274,7 @@ int run_fp8(const void* q, const void* k, const void* v, float q_scale, float k_
     return fail(FA_ERR_INVALID_ARG, "the FP8 scales must be finite and > 0 (q %g, k %g, v %g)", (double)q_scale,
                 (double)k_scale, (double)v_scale);
   const double c = (double)scale * q_scale * k_scale;
-  if (!(c < 1e30))
+  if (!(std::fabs(c) < 1e30))
     return fail(FA_ERR_INVALID_ARG, "scale * q_scale * k_scale = %g is out of range", c);
   if (!q || !k || !v || !o)
     return fail(FA_ERR_INVALID_ARG, "null q/k/v/o pointer");
@@ -368,7 +364,7 @@ uint64_t kvcache_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, 
 int run_kvcache(const void* q, const void* k, const void* v, const int* block_table, const int* seqlens, void* o,
                 float* lse, float* workspace, int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_pages,
                 int page_size, int max_pages, int causal, int window_left, float scale, int num_splits,
-                void* stream, fa_dtype_t dtype, bool paged) {
+                void* stream, int dtype, bool paged) {
   g_last_error[0] = '\0';
   if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
     return fail(FA_ERR_UNSUPPORTED, "the key/value-cache path supports bf16 and fp16 only (dtype %d)",
@@ -383,7 +379,6 @@ int run_kvcache(const void* q, const void* k, const void* v, const int* block_ta
     return fail(FA_ERR_INVALID_ARG, "Hq=%d must be a positive multiple of Hkv=%d", Hq, Hkv);
   if (window_left < -1) return fail(FA_ERR_INVALID_ARG, "window_left=%d (must be -1 or >= 0)", window_left);
   if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale is not finite");
-  if (!(scale > 0.f)) return fail(FA_ERR_UNSUPPORTED, "scale=%g: only positive scales are supported", (double)scale);
   if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d (supported: 64, 128)", d);
   if (paged && page_size != 16 && page_size % 32 != 0)
     return fail(FA_ERR_UNSUPPORTED, "page_size=%d must be 16 or a multiple of 32", page_size);
@@ -465,7 +460,7 @@ int run_kvcache(const void* q, const void* k, const void* v, const int* block_ta
   p.page_size = paged ? page_size : 0;
   p.max_pages = paged ? max_pages : 0;
   p.num_pages = paged ? num_pages : 0;
-  p.scale_log2 = scale * 1.4426950408889634f;
+  fa::set_score_scale(p, scale);
   const hipError_t e = fa::launch_decode(p, d, dtype == FA_DTYPE_F16, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return FA_OK;
@@ -477,7 +472,7 @@ uint64_t bwd_workspace_bytes(int B, int Hq, int N) {
 
 int run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
             void* dq, void* dk, void* dv, float* work, int B, int Hq, int Hkv, int N, int d, int causal,
-            int window_left, float scale, void* stream, fa_dtype_t dtype) {
+            int window_left, float scale, void* stream, int dtype) {
   g_last_error[0] = '\0';
   bool empty;
   if (int st = check_sizes(B, Hq, Hkv, N, d, window_left, scale, dtype, &empty)) return st;
@@ -543,7 +538,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
 extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-           int N, int d, int causal, int window_left, float scale, void* stream, fa_dtype_t dtype) {
+           int N, int d, int causal, int window_left, float scale, void* stream, int dtype) {
   return run(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window_left, scale, stream, dtype);
 }
 
@@ -565,7 +560,7 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens_q,
                   const int* cu_seqlens_k, int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
                   int max_seqlen_k, int d, int causal, int window_left, float scale, void* stream,
-                  fa_dtype_t dtype) {
+                  int dtype) {
   return run_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q, total_k, max_seqlen_q,
                     max_seqlen_k, d, causal, window_left, scale, stream, dtype);
 }
@@ -578,7 +573,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float
 
 int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, const int* cache_seqlens, void* o,
                    float* lse, float* workspace, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
-                   int window_left, float scale, int num_splits, void* stream, fa_dtype_t dtype) {
+                   int window_left, float scale, int num_splits, void* stream, int dtype) {
   return run_kvcache(q, k_cache, v_cache, nullptr, cache_seqlens, o, lse, workspace, B, Hq, Hkv, Nq, Nk, d, 0, 0, 0,
                      causal, window_left, scale, num_splits, stream, dtype, false);
 }
@@ -586,7 +581,7 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, cons
 int fa_fwd_kvcache_paged(const void* q, const void* k_pages, const void* v_pages, const int* block_table,
                          const int* cache_seqlens, void* o, float* lse, float* workspace, int B, int Hq, int Hkv,
                          int Nq, int d, int num_pages, int page_size, int max_pages_per_seq, int causal,
-                         int window_left, float scale, int num_splits, void* stream, fa_dtype_t dtype) {
+                         int window_left, float scale, int num_splits, void* stream, int dtype) {
   return run_kvcache(q, k_pages, v_pages, block_table, cache_seqlens, o, lse, workspace, B, Hq, Hkv, Nq, 0, d,
                      num_pages, page_size, max_pages_per_seq, causal, window_left, scale, num_splits, stream, dtype,
                      true);
@@ -655,7 +650,7 @@ size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
            void* dq, void* dk, void* dv, float* workspace, int B, int Hq, int Hkv, int N, int d, int causal,
-           int window_left, float scale, void* stream, fa_dtype_t dtype) {
+           int window_left, float scale, void* stream, int dtype) {
   return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, causal, window_left, scale,
                  stream, dtype);
 }
@@ -663,7 +658,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                   void* dq, void* dk, void* dv, float* workspace, const int* cu_seqlens_q, const int* cu_seqlens_k,
                   int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
-                  int causal, int window_left, float scale, void* stream, fa_dtype_t dtype) {
+                  int causal, int window_left, float scale, void* stream, int dtype) {
   return run_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv,
                         total_q, total_k, max_seqlen_q, max_seqlen_k, d, causal, window_left, scale, stream, dtype);
 }

@@ -54,6 +54,8 @@
 extern "C" {
 #endif
 
+/* Element types.  Entry points take the type as a plain int holding one of
+ * these values (any other int is rejected with FA_ERR_UNSUPPORTED). */
 typedef enum {
   FA_DTYPE_F32 = 0,   /* IEEE binary32 */
   FA_DTYPE_F16 = 1,   /* IEEE binary16 */
@@ -64,8 +66,8 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1, /* null pointer, negative size, Hq % Hkv != 0,
                               window_left < -1, non-finite scale          */
-  FA_ERR_UNSUPPORTED = -2, /* d not 64 or 128, unknown dtype, scale <= 0,
-                              one head's K or V of 2 GiB or more          */
+  FA_ERR_UNSUPPORTED = -2, /* d not 64 or 128, unknown dtype, one head's
+                              K or V of 2 GiB or more                     */
   FA_ERR_MISALIGNED = -3,  /* q, k, v or o not 16-byte aligned, lse not
                               4-byte aligned                              */
   FA_ERR_HIP = -4          /* the HIP runtime reported an error at launch */
@@ -83,8 +85,9 @@ typedef enum {
  *   causal       nonzero: key j is hidden from query i when j > i.
  *   window_left  -1: no window.  >= 0: key j is hidden from query i when
  *                j < i - window_left.  Composes with `causal`.
- *   scale        multiplier on q.k before the softmax; finite and > 0
- *                (the usual value is 1/sqrt(d)).
+ *   scale        multiplier on q.k before the softmax; any finite value
+ *                (the usual one is 1/sqrt(d); a negative scale favours
+ *                dissimilar keys, zero gives the mean of the visible V rows).
  *   stream       hipStream_t to enqueue on, NULL for the null stream.
  *
  * If B, Hq or N is 0 the call does nothing and returns FA_OK (pointers are
@@ -93,7 +96,7 @@ typedef enum {
  */
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            int B, int Hq, int Hkv, int N, int d, int causal, int window_left,
-           float scale, void *stream, fa_dtype_t dtype);
+           float scale, void *stream, int dtype);
 
 /* The same operation with the element type fixed by the name. */
 int fa_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -127,9 +130,15 @@ int fa_fwd_f32(const void *q, const void *k, const void *v, void *o, float *lse,
  *                 total_q / total_k (the kernel clamps them into range, so
  *                 inconsistent offsets give unspecified values, never an
  *                 access outside the tensors).
- *   max_seqlen_q, max_seqlen_k  upper bounds of Lq and Lk over the batch;
- *                 query rows beyond max_seqlen_q are not computed.
+ *   max_seqlen_q, max_seqlen_k  upper bounds of Lq and Lk over the batch
+ *                 (a smaller value leaves a longer sequence's query rows from
+ *                 max_seqlen_q on unwritten and its other rows unspecified,
+ *                 never an access outside the tensors).
  *   B, Hq, Hkv, d, causal, window_left, scale, stream  as for fa_fwd.
+ *
+ * Rows of o and lse that no sequence owns (from cu_seqlens_q[B] to total_q)
+ * are left exactly as the caller passed them: the call writes only the rows
+ * of the sequences.
  *
  * Errors as for fa_fwd; FA_DTYPE_F32 is FA_ERR_UNSUPPORTED; max_seqlen_k * Hkv
  * * d * 2 bytes must stay below 2 GiB.
@@ -137,7 +146,7 @@ int fa_fwd_f32(const void *q, const void *k, const void *v, void *o, float *lse,
 int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
                   const int *cu_seqlens_q, const int *cu_seqlens_k, int B, int Hq, int Hkv,
                   int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
-                  int causal, int window_left, float scale, void *stream, fa_dtype_t dtype);
+                  int causal, int window_left, float scale, void *stream, int dtype);
 
 /*
  * Attention forward on FP8 inputs with per-tensor scales.
@@ -227,7 +236,7 @@ int fa_fwd_kvcache(const void *q, const void *k_cache, const void *v_cache,
                    const int *cache_seqlens, void *o, float *lse, float *workspace,
                    int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                    int window_left, float scale, int num_splits, void *stream,
-                   fa_dtype_t dtype);
+                   int dtype);
 
 /*
  * The same operation on a paged cache: the keys of batch b are spread over
@@ -249,7 +258,7 @@ int fa_fwd_kvcache_paged(const void *q, const void *k_pages, const void *v_pages
                          float *lse, float *workspace, int B, int Hq, int Hkv, int Nq,
                          int d, int num_pages, int page_size, int max_pages_per_seq,
                          int causal, int window_left, float scale, int num_splits,
-                         void *stream, fa_dtype_t dtype);
+                         void *stream, int dtype);
 
 /* Splits fa_fwd_kvcache uses when num_splits = 0 (enough parallel work for
  * the current device, at least four 32-key tiles per split); 1 for sizes
@@ -313,7 +322,7 @@ size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
            const void *dout, void *dq, void *dk, void *dv, float *workspace,
            int B, int Hq, int Hkv, int N, int d, int causal, int window_left,
-           float scale, void *stream, fa_dtype_t dtype);
+           float scale, void *stream, int dtype);
 int fa_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const float *lse,
                 const void *dout, void *dq, void *dk, void *dv, float *workspace,
                 int B, int Hq, int Hkv, int N, int d, int causal, int window_left,
@@ -352,7 +361,7 @@ int fa_bwd_varlen(const void *q, const void *k, const void *v, const void *o, co
                   const void *dout, void *dq, void *dk, void *dv, float *workspace,
                   const int *cu_seqlens_q, const int *cu_seqlens_k, int B, int Hq, int Hkv,
                   int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d,
-                  int causal, int window_left, float scale, void *stream, fa_dtype_t dtype);
+                  int causal, int window_left, float scale, void *stream, int dtype);
 
 /* Bytes of workspace fa_bwd needs: 2 * B * Hq * N * sizeof(float) (0 when
  * any size is 0 or negative); fa_bwd_varlen takes B = 1, N = total_q. */

@@ -67,8 +67,6 @@ def call(dtype=_lib.FA_DTYPE_BF16, **over):
     (dict(window_left=-2), _lib.FA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), _lib.FA_ERR_INVALID_ARG),
     (dict(scale=float("inf")), _lib.FA_ERR_INVALID_ARG),
-    (dict(scale=0.0), _lib.FA_ERR_UNSUPPORTED),
-    (dict(scale=-0.5), _lib.FA_ERR_UNSUPPORTED),
     (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
     (dict(d=256), _lib.FA_ERR_UNSUPPORTED),
     (dict(q=0), _lib.FA_ERR_INVALID_ARG),
@@ -82,6 +80,35 @@ def call(dtype=_lib.FA_DTYPE_BF16, **over):
 def test_validation_rejects(over, status):
     assert call(**over) == status
     assert _lib.fa_last_error() != ""
+
+
+def _nan_floats():
+    """NaNs by bit pattern (quiet, signalling, negative, with payloads) and
+    the infinities, as float32 objects that reach the C side bit for bit."""
+    import struct
+    bits = [0x7FC00000, 0x7F800001, 0xFFC00000, 0xFF800001, 0x7FFFFFFF, 0x7FA5A5A5, 0x7F800000, 0xFF800000]
+    return [ctypes.c_float.from_buffer_copy(struct.pack("<I", b)) for b in bits]
+
+
+@pytest.mark.parametrize("x", _nan_floats(), ids=lambda x: f"{ctypes.cast(ctypes.pointer(x), ctypes.POINTER(ctypes.c_uint32)).contents.value:#010x}")
+def test_non_finite_scale_by_bit_pattern(x):
+    """Every NaN and infinity is rejected whatever its bits: the host check
+    must not depend on floating-point semantics the compiler may assume away."""
+    assert call(scale=x) == _lib.FA_ERR_INVALID_ARG
+    assert call_bwd(scale=x) == _lib.FA_ERR_INVALID_ARG
+    assert call_fp8(scale=x) == _lib.FA_ERR_INVALID_ARG
+    assert call_fp8(vs=x) == _lib.FA_ERR_INVALID_ARG
+    assert call_kv(scale=x) == _lib.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0, -0.5, -1e-30, -3.0e4])
+def test_zero_and_negative_scales_pass_validation(scale):
+    """Any finite scale is accepted: paired with an unsupported head dimension
+    (so nothing is launched), the error reported is the head dimension's."""
+    for fn in (lambda: call(scale=scale, d=96), lambda: call_bwd(scale=scale, d=96),
+               lambda: call_fp8(scale=scale, d=96), lambda: call_kv(scale=scale, d=96)):
+        assert fn() == _lib.FA_ERR_UNSUPPORTED
+        assert "head dimension" in _lib.fa_last_error() and "scale" not in _lib.fa_last_error()
 
 
 def test_unknown_dtype():
@@ -126,7 +153,6 @@ def call_bwd(dtype=_lib.FA_DTYPE_BF16, **over):
     (dict(Hkv=3), _lib.FA_ERR_INVALID_ARG),
     (dict(window_left=-2), _lib.FA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), _lib.FA_ERR_INVALID_ARG),
-    (dict(scale=0.0), _lib.FA_ERR_UNSUPPORTED),
     (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
     (dict(lse=0), _lib.FA_ERR_INVALID_ARG),
     (dict(dout=0), _lib.FA_ERR_INVALID_ARG),
@@ -180,7 +206,6 @@ def call_fp8(**over):
     (dict(Hkv=3), _lib.FA_ERR_INVALID_ARG),
     (dict(window_left=-2), _lib.FA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), _lib.FA_ERR_INVALID_ARG),
-    (dict(scale=0.0), _lib.FA_ERR_UNSUPPORTED),
     (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
     (dict(qs=0.0), _lib.FA_ERR_INVALID_ARG),
     (dict(ks=-1.0), _lib.FA_ERR_INVALID_ARG),
@@ -223,7 +248,6 @@ def call_kv(dtype=_lib.FA_DTYPE_BF16, **over):
     (dict(Hkv=3), _lib.FA_ERR_INVALID_ARG),
     (dict(window_left=-2), _lib.FA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), _lib.FA_ERR_INVALID_ARG),
-    (dict(scale=0.0), _lib.FA_ERR_UNSUPPORTED),
     (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
     (dict(q=0), _lib.FA_ERR_INVALID_ARG),
     (dict(ws=0), _lib.FA_ERR_INVALID_ARG),                # two splits need a workspace
@@ -346,7 +370,9 @@ def call_vl(dtype=_lib.FA_DTYPE_BF16, **over):
     (dict(tk=-1), _lib.FA_ERR_INVALID_ARG),
     (dict(Hkv=3), _lib.FA_ERR_INVALID_ARG),
     (dict(window_left=-2), _lib.FA_ERR_INVALID_ARG),
-    (dict(scale=0.0), _lib.FA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0, d=80), _lib.FA_ERR_UNSUPPORTED),     # a zero scale passes; the head dimension does not
+    (dict(scale=-2.0, d=80), _lib.FA_ERR_UNSUPPORTED),
     (dict(d=80), _lib.FA_ERR_UNSUPPORTED),
     (dict(cq=0), _lib.FA_ERR_INVALID_ARG),
     (dict(ck=0), _lib.FA_ERR_INVALID_ARG),
@@ -387,7 +413,7 @@ def call_bvl(dtype=_lib.FA_DTYPE_BF16, **over):
     (dict(Hkv=3), _lib.FA_ERR_INVALID_ARG),
     (dict(window_left=-2), _lib.FA_ERR_INVALID_ARG),
     (dict(scale=float("inf")), _lib.FA_ERR_INVALID_ARG),
-    (dict(scale=-1.0), _lib.FA_ERR_UNSUPPORTED),
+    (dict(scale=-1.0, d=96), _lib.FA_ERR_UNSUPPORTED),    # a negative scale passes; the head dimension does not
     (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
     (dict(lse=0), _lib.FA_ERR_INVALID_ARG),
     (dict(work=0), _lib.FA_ERR_INVALID_ARG),
