@@ -8,13 +8,25 @@ them.  The oracle differentiates the exact forward.
 Bound (derived from the arithmetic of the kernels): the kernels round P (for
 dV) and dS (for dQ, dK) once to the input type, unit roundoff u (bf16 2^-8,
 fp16 2^-11), form D_i from the rounded forward output, and accumulate in fp32
-over up to N terms.  Per element,
+over up to n terms (n = N keys for dQ; n = G N query rows for dK and dV,
+whose key/value head is shared by the G query heads of its group).  Per
+element,
 
-    |got - ref| <= (2u + N 2^-24) (M + M_f) + u |ref| + 2^-100 max|ref|
+    |got - ref| <= (2u + n 2^-24 + e_P) (M + M_f) + s (M_v + 1) + u |ref| + 2^-100 max|ref|
 
-with M the same product over absolute values (|P|^T|dO|, scale |dS||K|,
-scale |dS|^T|Q|) and M_f the row-term product (zero for dV); both come from
-the oracle.  The last term is an absolute floor for probabilities that
+with M the same product over absolute values (|P|^T|dO|, |scale| |dS||K|,
+|scale| |dS|^T|Q|), M_f the row-term product (zero for dV) and M_v the
+product with the visibility matrix in place of P or dS (Vis^T|dO|,
+|scale| Vis|K|, |scale| Vis^T|Q|); all three come from the oracle.  s is the
+absolute rounding error of a value below the type's normal range (an entry
+of P or dS, or the stored gradient): fp16's subnormals (below 2^-14) are
+spaced 2^-24, so s = 2^-25 for fp16, while
+bfloat16 has fp32's exponent range (s = 0; the floor below covers it).
+e_P = 2 d 2^-24 S + (N + 8) 2^-24 + 2^-20 (17 + S + ln(N + 1)) is the
+relative error of the rebuilt P = exp(scale s - lse): the fp32 score of the
+backward and of the forward (d 2^-24 S each, S = |scale| max||q|| max||k||
+bounding every |scale| sum_c |q_c k_c|), the forward's fp32 row sum and
+the exp2, log and scale approximations.  The last term is an absolute floor for probabilities that
 underflow fp32 (scores more than ~87 units below their row's maximum), far
 below any visible contribution.  Mean errors are also reported.
 """
@@ -34,6 +46,10 @@ from workloads import WORKLOADS, make_grad, make_inputs, random_grad, random_inp
 pytestmark = pytest.mark.gpu
 
 UNIT = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+# largest absolute rounding error of a value below the type's normal range
+# (fp16 subnormals are spaced 2^-24; bf16 shares fp32's exponent range, where
+# the floor below covers it)
+SUBNORMAL_ABS = {"bf16": 0.0, "f16": 2.0 ** -25}
 
 
 def run_bwd_gpu(q, k, v, do, dtype, causal, wl, scale, label=""):
@@ -46,15 +62,29 @@ def run_bwd_gpu(q, k, v, do, dtype, causal, wl, scale, label=""):
 
 
 def check_grads(got, ref, mag, dtype, N, label=""):
+    """Every element of (dq, dk, dv) under the bound of the module doc.  N is
+    the longest sequence: dQ accumulates over up to N keys, dK and dV of a
+    key/value head over up to G * N query rows (the group's G query heads
+    share it), so the fp32 accumulation term counts those."""
     u = UNIT[dtype]
-    gamma = N * 2.0 ** -24
+    G = got[0].shape[1] // got[1].shape[1]   # heads sit on axis 1 in both layouts
+    terms = {"dq": N, "dk": G * N, "dv": G * N}
+    # relative error of the rebuilt probabilities: the backward's fp32 score
+    # and the forward's logsumexp (its score error, sum and log) enter
+    # exp(scale s - lse)
+    S, d = mag["score_size"], got[0].shape[-1]
+    e_p = 2 * d * 2.0 ** -24 * S + (N + 8) * 2.0 ** -24 + 2.0 ** -20 * (17 + S + np.log(N + 1))
     for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        gamma = terms[name] * 2.0 ** -24
         assert np.isfinite(g).all(), f"{label}: non-finite {name}"
         m = mag[name] + (mag[name + "_f"] if name + "_f" in mag else 0.0)
         # fp32 flushes probabilities below its range (scores ~100 units below
         # the row max): allow an absolute floor far below any visible value
         floor = 2.0 ** -100 * float(np.abs(r).max(initial=0))
-        bound = (2 * u + gamma) * m + u * np.abs(r) + floor
+        # a P or dS entry below the normal range is rounded with an absolute
+        # error: summed over the visible pairs (the oracle's visibility products)
+        sub = SUBNORMAL_ABS[dtype] * (mag[name + "_v"] + 1.0)   # ... and the stored gradient itself
+        bound = (2 * u + gamma + e_p) * m + sub + u * np.abs(r) + floor
         err = np.abs(g - r)
         worst = float((err / np.maximum(bound, 1e-300)).max(initial=0))
         rms = float(np.sqrt(np.mean(r ** 2))) if r.size else 0.0
@@ -64,8 +94,18 @@ def check_grads(got, ref, mag, dtype, N, label=""):
         assert (err <= bound).all(), f"{label}: {name} exceeds the bound (worst ratio {worst:.3f})"
 
 
+def score_size(q, k, scale):
+    """|scale| max_i ||q_i|| max_j ||k_j||: by Cauchy-Schwarz at least
+    |scale| sum_c |q_ic| |k_jc| for every (query, key) pair, i.e. a bound on
+    every score's size and on what its fp32 sum accumulates."""
+    nq = float(np.sqrt((np.asarray(q, np.float64) ** 2).sum(axis=-1)).max(initial=0.0))
+    nk = float(np.sqrt((np.asarray(k, np.float64) ** 2).sum(axis=-1)).max(initial=0.0))
+    return abs(scale) * nq * nk
+
+
 def oracle_grads(q, k, v, do, causal, wl, scale):
     dq, dk, dv, mag = attention_bwd(q, k, v, do, causal, wl, scale, bounds=True)
+    mag["score_size"] = score_size(q, k, scale)
     return (dq, dk, dv), mag
 
 
@@ -138,25 +178,21 @@ def test_bwd_workloads_reduced(name):
     check_grads(got, ref, mag, w.dtype, N, f"{name} reduced")
 
 
-# --- full sizes: every row of one key/value-head group, in the launch shape --
+# --- full sizes: every element, in the benchmark's launch shape -------------
 
 @pytest.mark.parametrize("name", ["causal_8k", "gqa_f16_4k"])
-def test_bwd_full_size_one_group(name):
-    """The whole problem runs at full size on the GPU; the oracle checks every
-    dq row of the last group's query heads and every dk, dv row of its shared
-    head."""
+def test_bwd_full_size_every_element(name):
+    """The whole problem at full size on the GPU; the oracle checks every
+    element of dq, dk and dv (its worker threads each hold BLAS to one
+    thread)."""
+    from threadpoolctl import threadpool_limits
     w = WORKLOADS[name]
     q, k, v = make_inputs(w)
     do = make_grad(w)
     got = run_bwd_gpu(q, k, v, do, w.dtype, w.causal, w.window_left, w.scale, f"{name} full")
-    G = w.Hq // w.Hkv
-    b, hk = w.B - 1, w.Hkv - 1
-    hs = slice(hk * G, hk * G + G)
-    sl = lambda x, s: x[b:b + 1, s]  # noqa: E731
-    ref, mag = oracle_grads(sl(q, hs), sl(k, slice(hk, hk + 1)), sl(v, slice(hk, hk + 1)), sl(do, hs),
-                            w.causal, w.window_left, w.scale)
-    got_g = (got[0][b:b + 1, hs], got[1][b:b + 1, hk:hk + 1], got[2][b:b + 1, hk:hk + 1])
-    check_grads(got_g, ref, mag, w.dtype, w.N, f"{name} full, batch {b} kv head {hk}")
+    with threadpool_limits(limits=1):
+        ref, mag = oracle_grads(q, k, v, do, w.causal, w.window_left, w.scale)
+    check_grads(got, ref, mag, w.dtype, w.N, f"{name} full, every element")
 
 
 # --- properties -------------------------------------------------------------

@@ -14,7 +14,7 @@ import torch
 import exact_tiled_attention_04_amd as fa
 from oracle import attention_bwd_varlen
 from tests.gpu_util import announce, to_dev
-from tests.test_bwd_gpu import check_grads
+from tests.test_bwd_gpu import check_grads, score_size
 from workloads import round_to
 
 pytestmark = pytest.mark.gpu
@@ -50,6 +50,7 @@ def run(q, k, v, do, cq, ck, causal, wl, scale, dtype, label, max_q=None, max_k=
 
 def check(got, q, k, v, do, cq, ck, causal, wl, scale, dtype, label):
     dq, dk, dv, mag = attention_bwd_varlen(q, k, v, do, cq, ck, causal, wl, scale, bounds=True)
+    mag["score_size"] = score_size(q, k, scale)
     n = max(int(np.diff(cq).max(initial=1)), int(np.diff(ck).max(initial=1)))
     check_grads(got, (dq, dk, dv), mag, dtype, n, label)
 
