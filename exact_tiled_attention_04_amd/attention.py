@@ -68,7 +68,9 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: 
     and cu_seqlens_k int32 [B+1] offsets on the GPU, max_seqlen_q and
     max_seqlen_k the longest lengths.  Each sequence's query rows stand at the
     end of its keys.  Returns (o like q, lse float32 [Hq, total_q]).
-    Asynchronous on ``stream``."""
+    Asynchronous on ``stream``.  The library writes only the rows it
+    computes; when this function allocates o and lse, the rows no sequence
+    owns (and rows beyond max_seqlen_q) hold o = 0 and lse = -inf."""
     if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or k.shape[2] != q.shape[2]:
         raise ValueError("q must be [total_q, Hq, d] and k, v [total_k, Hkv, d]")
     if q.dtype not in (torch.float16, torch.bfloat16) or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -86,15 +88,17 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: 
     B = cq.numel() - 1
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = out if out is not None else torch.empty_like(q)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.stream(s):
+        # rows the library does not compute must not read as uninitialised memory
+        o = out if out is not None else torch.zeros_like(q)
+        if lse is None and want_lse:
+            lse = torch.full((Hq, total_q), float("-inf"), dtype=torch.float32, device=q.device)
     if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or o.device != q.device:
         raise ValueError("out must be a contiguous tensor like q")
-    if lse is None and want_lse:
-        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
     if lse is not None and (lse.shape != (Hq, total_q) or lse.dtype != torch.float32
                             or not lse.is_contiguous() or lse.device != q.device):
         raise ValueError("lse must be a contiguous float32 [Hq, total_q] tensor")
-    s = stream if stream is not None else torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):
         status = _lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                     lse.data_ptr() if lse is not None else None, cq.data_ptr(), ck.data_ptr(),

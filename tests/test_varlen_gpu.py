@@ -106,15 +106,46 @@ def test_varlen_offsets_past_the_tensors_are_clamped():
     np.testing.assert_array_equal(l1, l2)
 
 
-def test_varlen_workload_sampled_sequences():
-    """The full packed workload runs on the GPU; the oracle checks a short,
-    a middle and the longest sequence in full."""
+def test_varlen_workload_every_sequence():
+    """The full packed workload in the benchmark's launch configuration,
+    every element of every sequence against the packed oracle (its worker
+    threads each hold BLAS to one thread)."""
+    from threadpoolctl import threadpool_limits
     w = VARLEN_WORKLOADS["varlen_causal_16"]
     q, k, v, cu = make_varlen_inputs(w)
     o, lse = run_varlen(q, k, v, cu, cu, w.causal, w.window_left, w.scale, w.dtype, "varlen_causal_16 full")
-    lens = np.diff(cu)
-    for b in [int(np.argmin(lens)), len(lens) // 2, int(np.argmax(lens))]:
-        a, z = int(cu[b]), int(cu[b + 1])
-        sub = np.array([0, z - a], dtype=np.int32)
-        check(o[a:z], lse[:, a:z], q[a:z], k[a:z], v[a:z], sub, sub, w.causal, w.window_left, w.scale, w.dtype,
-              f"varlen_causal_16 sequence {b} (L={z - a})")
+    with threadpool_limits(limits=1):
+        check(o, lse, q, k, v, cu, cu, w.causal, w.window_left, w.scale, w.dtype, "varlen_causal_16 every sequence")
+
+
+def test_varlen_rows_no_sequence_computes():
+    """Rows past cu_seqlens_q[B] (and, with a max_seqlen_q below a
+    sequence's length, that sequence's rows from max_seqlen_q on): the C call
+    leaves the caller's buffers there untouched (a NaN fill survives bit for
+    bit); buffers the binding allocates hold o = 0 and lse = -inf there.  The
+    sequences within the stated maxima are computed as usual."""
+    lq = [60, 200]
+    q, k, v, cq, ck = _draw(1650, "bf16", lq, lq, 4, 2, 64)
+    total_q = q.shape[0]
+    pad = 37
+    qp = np.concatenate([q, np.ones((pad,) + q.shape[1:], np.float32)])
+    qd, kd, vd = (to_dev(x, "bf16") for x in (qp, k, v))
+    cqd, ckd = torch.from_numpy(cq).cuda(), torch.from_numpy(ck).cuda()
+    announce("varlen rows no sequence computes")
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full((4, total_q + pad), float("nan"), dtype=torch.float32, device="cuda")
+    fa.fwd_varlen(qd, kd, vd, cqd, ckd, 128, 200, causal=True, scale=0.125, out=o, lse=lse)
+    o2, l2 = fa.fwd_varlen(qd, kd, vd, cqd, ckd, 128, 200, causal=True, scale=0.125)
+    torch.cuda.synchronize()
+    o, lse, o2, l2 = (x.double().cpu().numpy() for x in (o, lse, o2, l2))
+    untouched = np.zeros(total_q + pad, dtype=bool)
+    untouched[60 + 128:total_q] = True        # second sequence's rows from max_seqlen_q on
+    untouched[total_q:] = True                # rows no sequence owns
+    assert np.isnan(o[untouched]).all() and np.isnan(lse[:, untouched]).all()
+    assert (o2[untouched] == 0).all() and np.isneginf(l2[:, untouched]).all()
+    assert np.isfinite(o[~untouched]).all() and np.isfinite(lse[:, ~untouched]).all()
+    np.testing.assert_array_equal(o[~untouched], o2[~untouched])
+    np.testing.assert_array_equal(lse[:, ~untouched], l2[:, ~untouched])
+    # the first sequence (60 rows, within both maxima) is exact attention
+    sub = np.array([0, 60], dtype=np.int32)
+    check(o[:60], lse[:, :60], q[:60], k[:60], v[:60], sub, sub, True, -1, 0.125, "bf16", "first sequence")
