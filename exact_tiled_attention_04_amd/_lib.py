@@ -25,7 +25,7 @@ FA_ERR_MISALIGNED = -3
 FA_ERR_HIP = -4
 
 EXPORTED = ["fa_fwd", "fa_fwd_bf16", "fa_fwd_f16", "fa_fwd_f32", "fa_fwd_varlen", "fa_fwd_fp8", "fa_fwd_kvcache",
-            "fa_fwd_kvcache_paged", "fa_fwd_kvcache_num_splits", "fa_fwd_kvcache_num_splits_for_lengths",
+            "fa_fwd_kvcache_paged", "fa_fwd_kvcache_paged_noalloc", "fa_fwd_kvcache_num_splits", "fa_fwd_kvcache_num_splits_for_lengths",
             "fa_fwd_kvcache_workspace_size", "fa_bwd", "fa_bwd_varlen",
             "fa_bwd_bf16", "fa_bwd_f16", "fa_bwd_workspace_size", "fa_status_string", "fa_last_error", "fa_version"]
 
@@ -66,6 +66,8 @@ def load() -> ctypes.CDLL:
         lib.fa_fwd_kvcache.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, I]
         lib.fa_fwd_kvcache.restype = I
         lib.fa_fwd_kvcache_paged.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, P, I]
+        lib.fa_fwd_kvcache_paged_noalloc.restype = I
+        lib.fa_fwd_kvcache_paged_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, P, I]
         lib.fa_fwd_kvcache_paged.restype = I
         lib.fa_fwd_kvcache_num_splits.argtypes = [I, I, I, I, I]
         lib.fa_fwd_kvcache_num_splits.restype = I
@@ -145,6 +147,15 @@ def fa_fwd_kvcache_paged(q, k_pages, v_pages, block_table, cache_seqlens, o, lse
                                        _ptr(cache_seqlens), _ptr(o), _ptr(lse), _ptr(workspace), B, Hq, Hkv, Nq, d,
                                        num_pages, page_size, max_pages_per_seq, int(bool(causal)), window_left,
                                        scale, num_splits, _ptr(stream), dtype)
+
+
+def fa_fwd_kvcache_paged_noalloc(q, k_pages, v_pages, block_table, cache_seqlens, o, lse, B, Hq, Hkv, Nq, d,
+                                 num_pages, page_size, max_pages_per_seq, causal, window_left, scale, num_splits,
+                                 stream, dtype) -> int:
+    return load().fa_fwd_kvcache_paged_noalloc(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                               _ptr(cache_seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, d, num_pages,
+                                               page_size, max_pages_per_seq, int(bool(causal)), window_left, scale,
+                                               num_splits, _ptr(stream), dtype)
 
 
 def fa_fwd_kvcache_num_splits(B: int, Hq: int, Hkv: int, Nq: int, Nk: int) -> int:

@@ -364,7 +364,7 @@ uint64_t kvcache_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, 
 int run_kvcache(const void* q, const void* k, const void* v, const int* block_table, const int* seqlens, void* o,
                 float* lse, float* workspace, int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_pages,
                 int page_size, int max_pages, int causal, int window_left, float scale, int num_splits,
-                void* stream, int dtype, bool paged) {
+                void* stream, int dtype, bool paged, bool use_scratch = false) {
   g_last_error[0] = '\0';
   if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
     return fail(FA_ERR_UNSUPPORTED, "the key/value-cache path supports bf16 and fp16 only (dtype %d)",
@@ -398,8 +398,18 @@ int run_kvcache(const void* q, const void* k, const void* v, const int* block_ta
   const int nk = (int)cap;
   if (num_splits > 128) return fail(FA_ERR_UNSUPPORTED, "num_splits=%d (at most 128)", num_splits);
   const int splits = resolve_splits(B, Hq, Hkv, Nq, nk, num_splits);
-  if (splits > 1 && !workspace)
+  if (use_scratch) {
+    // the allocation-free form: the library's own scratch array, if it fits
+    // (its address is looked up once every other check has passed)
+    const uint64_t need = kvcache_workspace_bytes(B, Hq, Hkv, Nq, nk, d, splits);
+    if (need > fa::decode_scratch_bytes())
+      return fail(FA_ERR_UNSUPPORTED,
+                  "%d splits of %lld rows need %llu bytes of scratch, more than the %zu the library holds "
+                  "(use fewer splits or fa_fwd_kvcache_paged with a workspace)",
+                  splits, (long long)B * Hq * Nq, (unsigned long long)need, fa::decode_scratch_bytes());
+  } else if (splits > 1 && !workspace) {
     return fail(FA_ERR_INVALID_ARG, "%d splits need a workspace (fa_fwd_kvcache_workspace_size bytes)", splits);
+  }
   if (workspace && !aligned(workspace, 16)) return fail(FA_ERR_MISALIGNED, "the workspace must be 16-byte aligned");
   const uint64_t n_q = (uint64_t)B * Hq * Nq * d * 2;
   const uint64_t n_l = (uint64_t)B * Hq * Nq * sizeof(float);
@@ -410,7 +420,7 @@ int run_kvcache(const void* q, const void* k, const void* v, const int* block_ta
   if (lse && (overlap(lse, n_l, o, n_q) || overlap(lse, n_l, q, n_q) || overlap(lse, n_l, k, n_kv) ||
               overlap(lse, n_l, v, n_kv)))
     return fail(FA_ERR_INVALID_ARG, "lse overlaps o or an input");
-  if (splits > 1 && (overlap(workspace, n_w, o, n_q) || overlap(workspace, n_w, q, n_q) ||
+  if (!use_scratch && splits > 1 && (overlap(workspace, n_w, o, n_q) || overlap(workspace, n_w, q, n_q) ||
                      (lse && overlap(workspace, n_w, lse, n_l)) || overlap(workspace, n_w, k, n_kv) ||
                      overlap(workspace, n_w, v, n_kv)))
     return fail(FA_ERR_INVALID_ARG, "the workspace overlaps another buffer");
@@ -420,6 +430,13 @@ int run_kvcache(const void* q, const void* k, const void* v, const int* block_ta
   const long long row_items = (rb + rb_item - 1) / rb_item;
   const long long items = (long long)B * Hkv * row_items * splits;
   if (items > INT32_MAX / 2) return fail(FA_ERR_UNSUPPORTED, "B*Hkv*row items*splits=%lld is too many", items);
+  if (use_scratch) {
+    workspace = nullptr;
+    if (splits > 1) {
+      const hipError_t e = fa::decode_scratch(&workspace);
+      if (e != hipSuccess) return fail(FA_ERR_HIP, "scratch address: %s", hipGetErrorString(e));
+    }
+  }
 
   fa::DecodeParams p;
   p.q = q;
@@ -585,6 +602,15 @@ int fa_fwd_kvcache_paged(const void* q, const void* k_pages, const void* v_pages
   return run_kvcache(q, k_pages, v_pages, block_table, cache_seqlens, o, lse, workspace, B, Hq, Hkv, Nq, 0, d,
                      num_pages, page_size, max_pages_per_seq, causal, window_left, scale, num_splits, stream, dtype,
                      true);
+}
+
+int fa_fwd_kvcache_paged_noalloc(const void* q, const void* k_pages, const void* v_pages, const int* block_table,
+                                 const int* cache_seqlens, void* o, float* lse, int B, int Hq, int Hkv, int Nq, int d,
+                                 int num_pages, int page_size, int max_pages_per_seq, int causal, int window_left,
+                                 float scale, int num_splits, void* stream, int dtype) {
+  return run_kvcache(q, k_pages, v_pages, block_table, cache_seqlens, o, lse, nullptr, B, Hq, Hkv, Nq, 0, d,
+                     num_pages, page_size, max_pages_per_seq, causal, window_left, scale, num_splits, stream, dtype,
+                     true, true);
 }
 
 int fa_fwd_kvcache_num_splits(int B, int Hq, int Hkv, int Nq, int Nk) {

@@ -42,5 +42,9 @@ hipError_t launch_decode(const DecodeParams& p, int d, bool f16, hipStream_t str
 // blocks share every K and V tile read into LDS.
 int decode_row_blocks_per_item(int n_row_blocks);
 int decode_waves_per_workgroup();
+// The allocation-free entry point's scratch: its size in bytes, and its device
+// address on the current device (looked up once per device).
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(float** ptr);
 
 }  // namespace fa

@@ -43,6 +43,7 @@
 #include "fa_mfma_common.h"
 
 #include <climits>
+#include <mutex>
 
 namespace fa {
 namespace {
@@ -580,5 +581,35 @@ hipError_t launch_decode(const DecodeParams& p, int d, bool f16, hipStream_t str
 int decode_waves_per_workgroup() { return kWaves; }
 
 int decode_row_blocks_per_item(int n_row_blocks) { return n_row_blocks >= 2 && kMaxRowBlocks >= 2 ? 2 : 1; }
+
+// Scratch of the allocation-free decoding entry point: the splits' partial
+// outputs and logsumexps live in this file-scope device array instead of a
+// caller's workspace.  Each GPU the library runs on holds its own copy at its
+// own address until the process ends.  In host code the array's name is a
+// host-side stand-in, never a device address: the address every launch uses
+// comes from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+size_t decode_scratch_bytes() { return kDecodeScratchBytes; }
+
+hipError_t decode_scratch(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float*>(a);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 }  // namespace fa

@@ -260,6 +260,28 @@ int fa_fwd_kvcache_paged(const void *q, const void *k_pages, const void *v_pages
                          int causal, int window_left, float scale, int num_splits,
                          void *stream, int dtype);
 
+/*
+ * fa_fwd_kvcache_paged without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The splits' partial outputs and
+ * logsumexps go to a scratch array the library holds in device memory, 16 MiB
+ * per GPU (one copy on each GPU it runs on, held until the process ends), so
+ * splits * B * Hq * Nq * (d + 1) * 4 bytes must not exceed 16 MiB (with one
+ * split no scratch is used); a larger request returns FA_ERR_UNSUPPORTED and
+ * enqueues nothing.  The call allocates nothing.  Every slot of the scratch
+ * a call reads is written earlier in the same call, so nothing needs
+ * clearing; but all calls on one GPU share the array, so calls that can
+ * overlap on one GPU (different streams, no ordering between them) race and
+ * must not be issued.  Arguments, results and other errors as for
+ * fa_fwd_kvcache_paged; the first call on a device also looks up the
+ * array's address there (a failure is FA_ERR_HIP).
+ */
+int fa_fwd_kvcache_paged_noalloc(const void *q, const void *k_pages, const void *v_pages,
+                                 const int *block_table, const int *cache_seqlens, void *o,
+                                 float *lse, int B, int Hq, int Hkv, int Nq, int d, int num_pages,
+                                 int page_size, int max_pages_per_seq, int causal, int window_left,
+                                 float scale, int num_splits, void *stream, int dtype);
+
 /* Splits fa_fwd_kvcache uses when num_splits = 0 (enough parallel work for
  * the current device, at least four 32-key tiles per split); 1 for sizes
  * that compute nothing. */

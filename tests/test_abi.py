@@ -436,3 +436,49 @@ def test_bwd_varlen_f32_and_empty():
     assert call_bvl(B=0, q=0, k=0, v=0, o=0, lse=0, dout=0, dq=0, dk=0, dv=0, work=0, cq=0, ck=0) == _lib.FA_OK
     assert call_bvl(tq=0) == _lib.FA_OK
     assert call_bvl(mq=0) == _lib.FA_OK
+
+
+# allocation-free paged decoding: validation as for the paged entry point, and
+# a request beyond the library's scratch rejected before anything is enqueued
+def call_noalloc(**over):
+    a = dict(q=Q, k=K, v=V, bt=BT, seq=SQ, o=O, lse=L, B=1, Hq=4, Hkv=2, Nq=1, d=64, pages=8, ps=64, maxp=4,
+             causal=1, wl=-1, scale=0.125, splits=2, dtype=_lib.FA_DTYPE_BF16)
+    a.update(over)
+    return _lib.fa_fwd_kvcache_paged_noalloc(a["q"], a["k"], a["v"], a["bt"], a["seq"], a["o"], a["lse"], a["B"],
+                                             a["Hq"], a["Hkv"], a["Nq"], a["d"], a["pages"], a["ps"], a["maxp"],
+                                             a["causal"], a["wl"], a["scale"], a["splits"], None, a["dtype"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(B=-1), _lib.FA_ERR_INVALID_ARG),
+    (dict(splits=-1), _lib.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _lib.FA_ERR_INVALID_ARG),
+    (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
+    (dict(ps=48), _lib.FA_ERR_UNSUPPORTED),
+    (dict(pages=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(bt=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(q=Q + 8), _lib.FA_ERR_MISALIGNED),
+    (dict(o=Q), _lib.FA_ERR_INVALID_ARG),
+    (dict(dtype=_lib.FA_DTYPE_F32), _lib.FA_ERR_UNSUPPORTED),
+    (dict(splits=129), _lib.FA_ERR_UNSUPPORTED),
+])
+def test_kvcache_paged_noalloc_validation_rejects(over, status):
+    assert call_noalloc(**over) == status
+    assert _lib.fa_last_error() != ""
+
+
+def test_kvcache_paged_noalloc_rejects_more_than_its_scratch():
+    # 8 splits * 64 * 64 rows * (128 + 1) floats = 16.9 MB > 16 MiB
+    st = call_noalloc(B=64, Hq=64, Hkv=2, d=128, pages=64 * 64, maxp=64, splits=8)
+    assert st == _lib.FA_ERR_UNSUPPORTED
+    assert "scratch" in _lib.fa_last_error()
+    # the same request against the workspace form is only short of its workspace
+    st = _lib.fa_fwd_kvcache_paged(Q, K, V, BT, SQ, O, L, None, 64, 64, 2, 1, 128, 64 * 64, 64, 64, 1, -1, 0.125, 8,
+                                   None, _lib.FA_DTYPE_BF16)
+    assert st == _lib.FA_ERR_INVALID_ARG and "workspace" in _lib.fa_last_error()
+
+
+def test_kvcache_paged_noalloc_empty_is_a_noop():
+    assert call_noalloc(B=0, q=0, k=0, v=0, o=0, lse=0) == _lib.FA_OK
+    assert call_noalloc(Nq=0) == _lib.FA_OK
