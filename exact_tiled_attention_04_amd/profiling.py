@@ -227,6 +227,9 @@ def main():
                 util = mf / (tr["avg_us"] * 1e-6) / (args.peak * 1e12)
                 lines.append(f"  MFMA FLOPs from {mops} x 512 = {mf:.4e} per launch -> {100 * util:.1f}% of "
                              f"{args.peak} TFLOP/s over the trace's average duration")
+        if "TCC_HIT_sum" in a and "TCC_MISS_sum" in a:
+            hit, miss = statistics.mean(a["TCC_HIT_sum"]), statistics.mean(a["TCC_MISS_sum"])
+            lines.append(f"  L2 hit rate TCC_HIT / (TCC_HIT + TCC_MISS) = {100 * hit / max(1.0, hit + miss):.1f}%")
         if "SQ_LDS_BANK_CONFLICT" in a and "SQ_LDS_IDX_ACTIVE" in a:
             bc = statistics.mean(a["SQ_LDS_BANK_CONFLICT"]) / max(1.0, statistics.mean(a["SQ_LDS_IDX_ACTIVE"]))
             lines.append(f"  LDS bank-conflict cycles / LDS active cycles = {100 * bc:.2f}%")
