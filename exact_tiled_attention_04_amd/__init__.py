@@ -20,57 +20,18 @@ of ``include/fa.h``).  This package is a thin binding:
 """
 from ._lib import FaError, LIB_PATH, load  # noqa: F401
 
-
-def fwd(*args, **kwargs):
-    from .attention import fwd as _fwd
-    return _fwd(*args, **kwargs)
-
-
-def fwd_varlen(*args, **kwargs):
-    from .attention import fwd_varlen as _f
-    return _f(*args, **kwargs)
+# The torch-facing calls live in ``attention``, which imports torch; they are
+# resolved on first use so that ``_lib`` (and the ABI checks built on it)
+# works without importing torch.
+_TORCH_API = ("fwd", "fwd_varlen", "fwd_fp8", "fwd_kvcache", "fwd_kvcache_paged", "kvcache_num_splits",
+              "bwd", "bwd_varlen", "attend", "attend_varlen")
 
 
-def fwd_fp8(*args, **kwargs):
-    from .attention import fwd_fp8 as _fwd_fp8
-    return _fwd_fp8(*args, **kwargs)
+def __getattr__(name):
+    if name in _TORCH_API:
+        from . import attention
+        return getattr(attention, name)
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")
 
 
-def fwd_kvcache(*args, **kwargs):
-    from .attention import fwd_kvcache as _f
-    return _f(*args, **kwargs)
-
-
-def fwd_kvcache_paged(*args, **kwargs):
-    from .attention import fwd_kvcache_paged as _f
-    return _f(*args, **kwargs)
-
-
-def kvcache_num_splits(*args, **kwargs):
-    from .attention import kvcache_num_splits as _f
-    return _f(*args, **kwargs)
-
-
-def bwd(*args, **kwargs):
-    from .attention import bwd as _bwd
-    return _bwd(*args, **kwargs)
-
-
-def bwd_varlen(*args, **kwargs):
-    from .attention import bwd_varlen as _f
-    return _f(*args, **kwargs)
-
-
-def attend_varlen(*args, **kwargs):
-    from .attention import attend_varlen as _a
-    return _a(*args, **kwargs)
-
-
-def attend(*args, **kwargs):
-    from .attention import attend as _a
-    return _a(*args, **kwargs)
-
-
-__all__ = ["fwd", "fwd_varlen", "fwd_fp8", "fwd_kvcache", "fwd_kvcache_paged", "kvcache_num_splits", "bwd", "bwd_varlen",
-           "attend", "attend_varlen", "FaError",
-           "LIB_PATH", "load"]
+__all__ = list(_TORCH_API) + ["FaError", "LIB_PATH", "load"]

@@ -58,9 +58,9 @@ constexpr int kBR = kWaves * kRowsPerWave;  // query rows per workgroup
 #ifndef FA8_KEYS_PER_TILE
 #define FA8_KEYS_PER_TILE 64
 #endif
-// Three waves per SIMD at d = 128 (the register budget of 168 costs a few
-// spilled registers and still wins over two waves); d = 64 needs fewer
-// registers and reaches four either way.
+// Three waves per SIMD at d = 128 (a register budget of 168, met without
+// spilling by rebuilding lane-derived offsets where they are used); d = 64
+// needs fewer registers and reaches four either way.
 #ifndef FA8_WAVES_PER_SIMD
 #define FA8_WAVES_PER_SIMD 3
 #endif
@@ -160,6 +160,14 @@ __device__ __forceinline__ void copy_tile_async(__amdgpu_buffer_rsrc_t r, const 
   }
 }
 
+// The lane index through an empty asm statement: values derived from it are
+// then recomputed where they are used instead of being hoisted out of the
+// key loop and held in registers (or spilled) across it.
+__device__ __forceinline__ int opaque_lane(int lane) {
+  asm volatile("" : "+v"(lane));
+  return lane;
+}
+
 template <int D>
 struct LoopCtx {
   __amdgpu_buffer_rsrc_t rk, rv;
@@ -167,9 +175,10 @@ struct LoopCtx {
   int N, wl, t_beg, t_end;
   int wave, lane, l32, hh;
   int wq0, wq1;
-  int vis_lo;
-  unsigned vis_span;
-  int v_lane[Shape<D>::kOutTiles];  // byte offset of this lane's transposing V read, per output tile
+  int k_base;  // byte offset of chunk 2hh of the lane's K row (row l32 of the tile)
+  // byte offset of this lane's transposing V read for output tile 0; tile ct
+  // reads at v_base ^ 32 ct (the tile index occupies bits 5-6 alone)
+  int v_base;
   bool causal;
   float c;                          // scale * q_scale * k_scale * log2(e)
 };
@@ -183,19 +192,23 @@ struct RowState {
 };
 
 // Scores of key tile t: S^T = K Q^T; s[h] holds keys kBC*t + 32h .. +31.
+// The lane reads 16-byte chunks 4kc + 2hh and 4kc + 2hh + 1 of its row; the
+// three index bits are distinct, so the swizzled byte offset is
+// x.k_base ^ 64 kc ^ 16 (one register kept across the loop, two XORs a step).
 template <int D>
 __device__ __forceinline__ void tile_scores(const unsigned char* __restrict__ cK, const LoopCtx<D>& x,
                                             const RowState<D>& st, f32x16 (&s)[kHalves]) {
 #pragma unroll
   for (int h = 0; h < kHalves; ++h) s[h] = f32x16{};
+  const int kbase = opaque_lane(x.k_base);
 #pragma unroll
   for (int kc = 0; kc < Shape<D>::kSteps; ++kc) {
+    const int a_lo = kbase ^ (64 * kc);
+    const int a_hi = a_lo ^ 16;
 #pragma unroll
     for (int h = 0; h < kHalves; ++h) {
-      const int row = 32 * h + x.l32;
-      const int c0 = 4 * kc + 2 * x.hh;
-      const u32x4 lo = *(const u32x4*)(cK + row * D + ((c0 ^ k_swz<D>(row)) << 4));
-      const u32x4 hi = *(const u32x4*)(cK + row * D + (((c0 + 1) ^ k_swz<D>(row)) << 4));
+      const u32x4 lo = *(const u32x4*)(cK + a_lo + 32 * h * D);
+      const u32x4 hi = *(const u32x4*)(cK + a_hi + 32 * h * D);
       s[h] = mma8(join(lo, hi), st.qf[kc], s[h]);
     }
   }
@@ -204,19 +217,27 @@ __device__ __forceinline__ void tile_scores(const unsigned char* __restrict__ cK
 // Mask tile t where it crosses the causal diagonal, the window edge or the
 // sequence end for some row of the wavefront: key kb + off is visible iff
 // 0 <= kb + off - vis_lo <= vis_span.
+// The lane's visible range is rebuilt from its lane index each time (a few
+// vector operations on the rare masked tiles) rather than kept in registers
+// across the key loop, where three waves per SIMD leave none to spare.
 template <int D>
 __device__ __forceinline__ void tile_mask(const LoopCtx<D>& x, int t, f32x16 (&s)[kHalves]) {
   const int kb = t * kBC;
   const int ke = kb + kBC - 1;
   const bool need_mask = (ke >= x.N) || (x.causal && ke > x.wq0) || (x.wl >= 0 && kb < x.wq1 - x.wl);
   if (!need_mask) return;
-  const int base = kb - x.vis_lo + 4 * x.hh;
+  const int ln = opaque_lane(x.lane);
+  const int myq = x.wq0 + (ln & 31);
+  const int vis_lo = x.wl >= 0 ? max(0, myq - x.wl) : 0;
+  const int vis_hi = x.causal ? min(myq, x.N - 1) : x.N - 1;
+  const unsigned vis_span = (unsigned)(vis_hi - vis_lo);
+  const int base = kb - vis_lo + 4 * (ln >> 5);
 #pragma unroll
   for (int h = 0; h < kHalves; ++h) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int off = 32 * h + 8 * (i >> 2) + (i & 3);
-      s[h][i] = ((unsigned)(base + off) <= x.vis_span) ? s[h][i] : -INFINITY;
+      s[h][i] = ((unsigned)(base + off) <= vis_span) ? s[h][i] : -INFINITY;
     }
   }
 }
@@ -308,7 +329,8 @@ __device__ __forceinline__ void tile_pv(const unsigned char* __restrict__ vC, co
       i32x2 r[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        r[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vC + x.v_lane[ct] + (64 * b + 16 * q) * D));
+        r[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_i32x2*)(vC + (x.v_base ^ (32 * ct)) + (64 * b + 16 * q) * D));
       const i32x8 a = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
       st.oacc[ct] = mma8(a, pf[b], st.oacc[ct]);
     }
@@ -345,15 +367,16 @@ __device__ __forceinline__ void pipeline_step(const unsigned char* __restrict__ 
   const float alpha = tile_softmax<D>(x, st, s, pf);
   if (kHasPrev) {
     tile_pv<D>(vC, x, st, pf_prev);
-    // each PV product follows a slice of the softmax work; its four reads
-    // were issued one product earlier
+    // each PV product follows a small slice of the softmax work (eight
+    // vector operations per 64-key block: of 8 to 40 measured, the fastest);
+    // its four reads were issued one product earlier
     constexpr int kPv = kBlocks64 * S::kOutTiles;
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS read
 #pragma unroll
     for (int g = 0; g < kPv; ++g) {
       if (g + 1 < kPv) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 24 / kBlocks64, 0);      // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 8 / kBlocks64, 0);       // VALU
     }
   }
 #pragma unroll
@@ -383,6 +406,7 @@ __global__ void __launch_bounds__(kThreads, FA8_WAVES_PER_SIMD) fwd_fp8_kernel(F
   x.l32 = x.lane & 31;
   x.hh = x.lane >> 5;
   x.off.init(x.wave, x.lane);
+  x.k_base = x.l32 * D + (((2 * x.hh) ^ k_swz<D>(x.l32)) << 4);
 
   const WorkItem it = decode_work_item(p, blockIdx.x);
   const int N = p.N;
@@ -412,9 +436,6 @@ __global__ void __launch_bounds__(kThreads, FA8_WAVES_PER_SIMD) fwd_fp8_kernel(F
   x.t_beg = kbeg / kBC;
   x.t_end = (kend + kBC - 1) / kBC;
 
-  x.vis_lo = x.wl >= 0 ? max(0, myq - x.wl) : 0;
-  const int vis_hi = x.causal ? min(myq, N - 1) : N - 1;
-  x.vis_span = (unsigned)(vis_hi - x.vis_lo);
 
   // Transposing V read: in each 16-lane group G, lane s = 2e + j supplies the
   // address for byte e of the group's outputs (key row 8(e/4) + 4(G/2) + e%4
@@ -424,8 +445,7 @@ __global__ void __launch_bounds__(kThreads, FA8_WAVES_PER_SIMD) fwd_fp8_kernel(F
     const int e = s16 >> 1, j = s16 & 1, g = x.lane >> 4;
     const int row = 8 * (e >> 2) + 4 * (g >> 1) + (e & 3);
     const int f = v_quad_swz<D>(row);  // the same for every 16-row slab
-#pragma unroll
-    for (int ct = 0; ct < S::kOutTiles; ++ct) x.v_lane[ct] = row * D + 32 * (ct ^ f) + 16 * (g & 1) + 8 * j;
+    x.v_base = row * D + 32 * f + 16 * (g & 1) + 8 * j;
   }
 
   RowState<D> st;
@@ -479,20 +499,23 @@ __global__ void __launch_bounds__(kThreads, FA8_WAVES_PER_SIMD) fwd_fp8_kernel(F
   float llo, lhi;
   half_pair(st.l_run, llo, lhi);
   const float l_tot = llo + lhi;
-  if (myq < N) {
+  const int ln = opaque_lane(x.lane);
+  const int hh = ln >> 5;
+  const int myq_out = x.wq0 + (ln & 31);
+  if (myq_out < N) {
     const float inv = p.o_mult / l_tot;
-    unsigned short* og = (unsigned short*)p.o + q_head + (long long)myq * D;
+    unsigned short* og = (unsigned short*)p.o + q_head + (long long)myq_out * D;
 #pragma unroll
     for (int ct = 0; ct < S::kOutTiles; ++ct) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const u32x2 w = u32x2{Bf16::pack2(st.oacc[ct][4 * gq + 0] * inv, st.oacc[ct][4 * gq + 1] * inv),
                               Bf16::pack2(st.oacc[ct][4 * gq + 2] * inv, st.oacc[ct][4 * gq + 3] * inv)};
-        *(u32x2*)(og + 32 * ct + 8 * gq + 4 * x.hh) = w;
+        *(u32x2*)(og + 32 * ct + 8 * gq + 4 * hh) = w;
       }
     }
-    if (x.hh == 0 && p.lse != nullptr)
-      p.lse[(long long)it.bh * N + myq] = (st.m_use - kPOffset + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    if (hh == 0 && p.lse != nullptr)
+      p.lse[(long long)it.bh * N + myq_out] = (st.m_use - kPOffset + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
 }
 
