@@ -19,8 +19,9 @@
 // sum_j P_ij dP_ij, the row term of the softmax Jacobian.
 //
 // Three launches, no atomics, bit-reproducible:
-//   1. prep: D_i and lse_i * log2(e) for every row, into the caller's
-//      workspace;
+//   1. prep: -D_i and lse_i * log2(e) for every row, into the caller's
+//      workspace (-D starts the dP accumulators, which then come out of the
+//      matrix cores as dP - D);
 //   2. dK/dV: one workgroup per (batch, key/value head, block of 128 keys);
 //      each group of its wavefronts owns 32 keys, takes their K and V rows as
 //      MFMA operands (from registers at d = 64, from LDS at d = 128) and keeps
@@ -187,8 +188,7 @@ __device__ __forceinline__ u32x4 tr_operand(const unsigned short* __restrict__ t
 // 16-byte rows) with the wavefront's own rows held as B operands.
 template <typename E, int D>
 __device__ __forceinline__ f32x16 rows_times_own(const unsigned short* __restrict__ t, int h, int l32, int hh,
-                                                 const u32x4* own) {
-  f32x16 acc = f32x16{};
+                                                 const u32x4* own, f32x16 acc = f32x16{}) {
 #pragma unroll
   for (int kc = 0; kc < Shape<D>::kSteps; ++kc) {
     const u32x4 a = *(const u32x4*)(t + row_off<D>(32 * h + l32, 2 * kc + hh));
@@ -232,7 +232,7 @@ __device__ __forceinline__ void pack_operands(const float* x, u32x4* dst) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. Row terms: D_i = sum_c dO_ic O_ic (fp32) and lse_i * log2(e).
+// 1. Row terms: -D_i = -sum_c dO_ic O_ic (fp32) and lse_i * log2(e).
 
 template <typename E>
 __device__ __forceinline__ float dot8(u32x4 a, u32x4 b);
@@ -282,7 +282,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p) {
       const long long t = row / p.Hq;
       idx = (row - t * p.Hq) * p.total_q + t;
     }
-    p.delta[idx] = s;
+    p.delta[idx] = -s;  // stored negated: it initialises the dP accumulators
     // a row that saw no key (lse = -inf) gets P = exp2(s - inf) = 0
     const float l = p.lse[idx];
     p.lse2[idx] = l == -INFINITY ? INFINITY : l * kLog2e;
@@ -320,10 +320,10 @@ __device__ __forceinline__ void scores_from_lds(const unsigned short* __restrict
                                                 const unsigned short* __restrict__ to,
                                                 const unsigned short* __restrict__ kk,
                                                 const unsigned short* __restrict__ vk, int own_row0, int qh,
-                                                int l32, int hh, f32x16& s, f32x16& dp) {
+                                                int l32, int hh, f32x16& s, f32x16& dp, const f32x16& dp0) {
   constexpr int kS = Shape<D>::kSteps;
   s = f32x16{};
-  dp = f32x16{};
+  dp = dp0;
 #pragma unroll
   for (int kc = 0; kc < kS; ++kc) {
     const u32x4 aq = *(const u32x4*)(tq + row_off<D>(32 * qh + l32, 2 * kc + hh));
@@ -469,26 +469,34 @@ __global__ void __launch_bounds__(kDkvThreads) bwd_dkdv_kernel(BwdParams p) {
     if (any) {
       const bool need_mask = qs + 32 > Nq || kw0 + kRows > Nk || (p.causal && qs + shift < kw0 + kRows - 1) ||
                              (wl >= 0 && qs + 31 + shift > kw0 + wl);
-      f32x16 s, dp;  // S[query][key], dP[query][key]
+      // the dP accumulators start from -D of their rows, so they come out
+      // as dP - D (element 4m+e is query row 8m + 4hh + e of the half)
+      f32x16 s, dp, dp0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float4 nd = *(const float4*)(&sD[buf][32 * qh + 8 * m + 4 * hh]);
+        dp0[4 * m] = nd.x;
+        dp0[4 * m + 1] = nd.y;
+        dp0[4 * m + 2] = nd.z;
+        dp0[4 * m + 3] = nd.w;
+      }
       if constexpr (kKvInLds<D>) {
-        scores_from_lds<E, D>(sQ[buf], sO[buf], sKk, sVk, kg * kRows, qh, l32, hh, s, dp);
+        scores_from_lds<E, D>(sQ[buf], sO[buf], sKk, sVk, kg * kRows, qh, l32, hh, s, dp, dp0);
       } else {
         s = rows_times_own<E, D>(sQ[buf], qh, l32, hh, kf);
-        dp = rows_times_own<E, D>(sO[buf], qh, l32, hh, vf);
+        dp = rows_times_own<E, D>(sO[buf], qh, l32, hh, vf, dp0);
       }
       float pv[16], dsv[16];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int r = 32 * qh + 8 * m + 4 * hh;  // tile row of elements 4m .. 4m+3
         const float4 l2 = *(const float4*)(&sL[buf][r]);
-        const float4 dd = *(const float4*)(&sD[buf][r]);
         const float l2v[4] = {l2.x, l2.y, l2.z, l2.w};
-        const float ddv[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * m + e;
           pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -l2v[e]));
-          dsv[i] = pv[i] * (dp[i] - ddv[e]);
+          dsv[i] = pv[i] * dp[i];
         }
       }
       if (need_mask) {
@@ -612,7 +620,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p) {
   load_own_row<D>((const unsigned short*)p.q + q_head + (long long)myq * q_rs, myq < Nq, hh, qf);
   load_own_row<D>((const unsigned short*)p.dout + q_head + (long long)myq * q_rs, myq < Nq, hh, of);
   const float l2 = myq < Nq ? p.lse2[vec0 + myq] : INFINITY;  // rows past the end: P = 0
-  const float dd = myq < Nq ? p.delta[vec0 + myq] : 0.f;
+  const float nd = myq < Nq ? p.delta[vec0 + myq] : 0.f;  // -D
   f32x16 dq[S::kOutTiles];
 #pragma unroll
   for (int ct = 0; ct < S::kOutTiles; ++ct) dq[ct] = f32x16{};
@@ -657,12 +665,15 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const f32x16 s = rows_times_own<E, D>(sK[buf], h, l32, hh, qf);   // S^T[key][query]
-        const f32x16 dp = rows_times_own<E, D>(sV[buf], h, l32, hh, of);  // dP^T[key][query]
+        f32x16 dp0;  // -D of the lane's query: the accumulators come out as dP - D
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dp0[i] = nd;
+        const f32x16 dp = rows_times_own<E, D>(sV[buf], h, l32, hh, of, dp0);  // (dP - D)^T[key][query]
         float dsv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.scale_log2, -l2));
-          float de = pe * (dp[i] - dd);
+          float de = pe * dp[i];
           if (need_mask) {
             const int key = kb + 32 * h + 8 * (i >> 2) + 4 * hh + (i & 3);
             de = (unsigned)(key - vis_lo) <= vis_span ? de : 0.f;

@@ -163,7 +163,7 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // [B][Hq][N] (packed: [Hq][total_q]): sum_c dout * o
+  float* delta;  // [B][Hq][N] (packed: [Hq][total_q]): -sum_c dout * o
   float* lse2;   // same layout: lse * log2(e), +inf where lse = -inf
   long long rows;  // B * Hq * N (packed: Hq * total_q)
   int B, Hq, Hkv, N;  // packed: N = max_seqlen_q
