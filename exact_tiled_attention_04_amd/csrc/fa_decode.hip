@@ -304,8 +304,12 @@ __global__ void __launch_bounds__(kWaves * kWaveSize) decode_split_kernel(Decode
   // the wavefront's rows need (a chunk size fixed on the host from the
   // cache capacity, so short sequences leave their last splits empty and no
   // split of a long one is longer than any other)
-  wlo = wave_min(wlo);
-  whi = wave_max(whi);
+  // (the reductions leave the same value in every lane; readfirstlane makes
+  // that known to the compiler, so the tile loop and every copy's buffer
+  // resource and offset stay in scalar registers instead of being wrapped in
+  // a loop over the distinct values of the lanes)
+  wlo = __builtin_amdgcn_readfirstlane(wave_min(wlo));
+  whi = __builtin_amdgcn_readfirstlane(wave_max(whi));
   int t_beg = 0, t_end = 0;
   if (whi >= wlo) {
     const int tb0 = wlo / kTile, tb1 = whi / kTile + 1;
