@@ -14,8 +14,8 @@
 //     blocks of 32 query rows, split of the key range).  The rows of a work
 //     item are all G * Nq query rows of the GQA group that shares the
 //     key/value head, so each cached key is read once per group, not once
-//     per query head; a group of more than 32 rows gives a wavefront two
-//     blocks, whose products share each K and V read from LDS;
+//     per query head; a group of four, six, ... blocks gives a wavefront
+//     two blocks, whose products share each K and V read from LDS;
 //   * the visible key range of a (batch, head) is cut into equal splits so
 //     that the grid holds enough wavefronts to keep HBM busy even for one
 //     sequence; each split writes its normalised partial output and its
@@ -62,9 +62,9 @@ constexpr int kTile = 32;  // keys per tile
 #endif
 constexpr int kWaves = FA_DEC_WAVES;    // independent wavefronts per workgroup
 constexpr int kStages = FA_DEC_STAGES;  // K/V tiles in LDS per wavefront
-// A GQA group of more than 32 query rows (G * Nq > 32) gives each wavefront
-// two 32-row blocks, so that every K and V tile it copies into LDS and reads
-// from there serves 64 rows.
+// A GQA group with an even number (at least four) of 32-row blocks gives each
+// wavefront two of them, so that every K and V tile it copies into LDS and
+// reads from there serves 64 rows (decode_row_blocks_per_item).
 #ifndef FA_DEC_MAX_RB
 #define FA_DEC_MAX_RB 2
 #endif
@@ -584,7 +584,15 @@ hipError_t launch_decode(const DecodeParams& p, int d, bool f16, hipStream_t str
 
 int decode_waves_per_workgroup() { return kWaves; }
 
-int decode_row_blocks_per_item(int n_row_blocks) { return n_row_blocks >= 2 && kMaxRowBlocks >= 2 ? 2 : 1; }
+// Two blocks per wavefront only for an even count of at least four: on
+// MI355X (16k-token caches, GQA 4:1, each count at the split count its own
+// rule picks) one block per wavefront was 5-12% faster for 2, 3 and 5 blocks
+// (more wavefronts, fewer registers each, no half-empty wavefront) and two
+// were 1-7% faster for 4 and 8 (each K/V tile copied into LDS once for 64
+// rows instead of 32).
+int decode_row_blocks_per_item(int n_row_blocks) {
+  return n_row_blocks >= 4 && n_row_blocks % 2 == 0 && kMaxRowBlocks >= 2 ? 2 : 1;
+}
 
 // Scratch of the allocation-free decoding entry point: the splits' partial
 // outputs and logsumexps live in this file-scope device array instead of a

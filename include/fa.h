@@ -293,8 +293,9 @@ int fa_fwd_kvcache_num_splits(int B, int Hq, int Hkv, int Nq, int Nk);
  * covers a fixed share of the capacity, short sequences leave their last
  * splits empty; this counts the splits that will read keys and takes the
  * fewest that give about three streaming wavefronts per compute unit (four
- * when a GQA group's G * Nq query rows exceed 32, so that one wavefront
- * takes two 32-row blocks) while keeping every work item in one wave of the
+ * when a GQA group's G * Nq query rows make an even number, at least four,
+ * of 32-row blocks, so that one wavefront takes two of them) while keeping
+ * every work item in one wave of the
  * grid (at most four per unit), else the fewest splits that put the most
  * work items in that wave; at least four 32-key tiles per split and at most
  * 128.  Equal full lengths give fewer splits than fa_fwd_kvcache_num_splits

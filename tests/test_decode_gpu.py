@@ -67,11 +67,14 @@ SHAPES = [
     # (Hq, Hkv, Nq, Nk, lens)
     (4, 2, 1, 100, [100, 1, 37, 64]),
     (8, 2, 3, 257, [257, 2, 0, 96]),
-    (8, 1, 5, 64, [64, 32, 3, 5]),        # G * Nq = 40: two row blocks
+    (8, 1, 5, 64, [64, 32, 3, 5]),        # G * Nq = 40: two row blocks, the second partly filled
     (32, 8, 16, 600, [600, 17, 300, 33]),  # G * Nq = 64
     (2, 2, 40, 130, [130, 40, 41, 128]),   # Nq > 32 on its own
-    (8, 1, 12, 200, [200, 150, 13, 0]),    # G * Nq = 96: a wavefront with one full and one empty block
+    (8, 1, 12, 200, [200, 150, 13, 0]),    # G * Nq = 96: three blocks
     (16, 1, 9, 160, [160, 31, 9, 100]),    # G * Nq = 144: five blocks, the last partly filled
+    # an even block count of at least four: two blocks per wavefront
+    (16, 2, 13, 200, [200, 77, 13, 1]),    # G * Nq = 104: four blocks, the last partly filled
+    (8, 1, 22, 96, [96, 40, 22, 64]),      # G * Nq = 176: six blocks, the last half filled
 ]
 
 
