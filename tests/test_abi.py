@@ -326,13 +326,16 @@ def test_kvcache_splits_for_lengths():
     rows = lambda Hq, Hkv, Nq: -(-(Hq // Hkv) * Nq // 32)
     # equal full caches: three streaming wavefronts per unit are enough
     assert _splits_for([32768] * 8, 32, 8, 1, 32768) == 12
-    # 16 query rows per sequence make two row blocks, which one wavefront
-    # takes together: four streams per unit
-    assert _splits_for([16384] * 4, 32, 8, 16, 16384) == 32
-    # three blocks make two work items per stream: four items per unit cap
-    # the splits first, at the fewest splits that reach the cap (32 to 34
-    # cut the same 32 chunks per sequence)
-    assert _splits_for([16384] * 4, 32, 4, 12, 16384) == 32
+    # 16 query rows per sequence make two row blocks, one work item each:
+    # four items per unit (64 per split) cap the splits at 16 before three
+    # streams per unit are reached
+    assert _splits_for([16384] * 4, 32, 8, 16, 16384) == 16
+    # three blocks, three items per stream: the cap of 1024 items allows 21
+    # splits (48 items each)
+    assert _splits_for([16384] * 4, 32, 4, 12, 16384) == 21
+    # four blocks: one wavefront takes two, two items per stream; the target
+    # is four streams per unit, and the cap stops it at 32 splits
+    assert _splits_for([16384] * 4, 32, 4, 16, 16384) == 32
     # caches of varied lengths leave splits empty: more splits than for full ones
     import numpy as np
     lens = np.random.default_rng(6).integers(1, 16385, 16)
