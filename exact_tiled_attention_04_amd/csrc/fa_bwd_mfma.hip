@@ -671,14 +671,16 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p) {
         const f32x16 dp = rows_times_own<E, D>(sV[buf], h, l32, hh, of, dp0);  // (dP - D)^T[key][query]
         float dsv[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.scale_log2, -l2));
-          float de = pe * dp[i];
-          if (need_mask) {
+        for (int i = 0; i < 16; ++i)
+          dsv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.scale_log2, -l2)) * dp[i];
+        // one branch around the whole block (a test per element would be
+        // turned into selects that every tile pays for)
+        if (need_mask) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
             const int key = kb + 32 * h + 8 * (i >> 2) + 4 * hh + (i & 3);
-            de = (unsigned)(key - vis_lo) <= vis_span ? de : 0.f;
+            dsv[i] = (unsigned)(key - vis_lo) <= vis_span ? dsv[i] : 0.f;
           }
-          dsv[i] = de;
         }
         u32x4 df[2];
         pack_operands<E>(dsv, df);
