@@ -282,6 +282,9 @@ __global__ void __launch_bounds__(kWaves * kWaveSize) decode_split_kernel(Decode
   unsigned span[kRB];
   long long out_row[kRB];
   int wlo = INT_MAX, whi = -1;
+  // keys every valid row of block j sees: [clean_lo[j], clean_hi[j]] (empty
+  // when some valid row sees no key); a tile inside it needs no mask
+  int clean_lo[kRB], clean_hi[kRB];
 #pragma unroll
   for (int j = 0; j < kRB; ++j) {
     const int r = (ri * kRB + j) * 32 + l32;
@@ -298,6 +301,8 @@ __global__ void __launch_bounds__(kWaves * kWaveSize) decode_split_kernel(Decode
       wlo = min(wlo, lo[j]);
       whi = max(whi, hi);
     }
+    clean_lo[j] = __builtin_amdgcn_readfirstlane(wave_max(valid[j] ? (any[j] ? lo[j] : INT_MAX) : INT_MIN));
+    clean_hi[j] = __builtin_amdgcn_readfirstlane(wave_min(valid[j] ? (any[j] ? hi : INT_MIN) : INT_MAX));
   }
 
   // this split's tiles: the s-th chunk of tiles_per_split tiles of the range
@@ -395,12 +400,16 @@ __global__ void __launch_bounds__(kWaves * kWaveSize) decode_split_kernel(Decode
       u32x4 pf[kRB][2];
 #pragma unroll
       for (int j = 0; j < kRB; ++j) {
-        // mask: key kb + 8(e/4) + 4hh + e%4 is visible iff lo <= key <= hi
-        const int base = t * kTile + 4 * hh - lo[j];
+        // mask: key kb + 8(e/4) + 4hh + e%4 is visible iff lo <= key <= hi;
+        // tiles every valid row sees whole skip it (rows past the group's
+        // are never stored)
+        if (t * kTile < clean_lo[j] || t * kTile + kTile - 1 > clean_hi[j]) {
+          const int base = t * kTile + 4 * hh - lo[j];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int off = 8 * (e >> 2) + (e & 3);
-          sacc[j][e] = (any[j] && (unsigned)(base + off) <= span[j]) ? sacc[j][e] : -INFINITY;
+          for (int e = 0; e < 16; ++e) {
+            const int off = 8 * (e >> 2) + (e & 3);
+            sacc[j][e] = (any[j] && (unsigned)(base + off) <= span[j]) ? sacc[j][e] : -INFINITY;
+          }
         }
         // online softmax (base 2, scale folded into the exponent)
         float mx = sacc[j][0];
