@@ -24,6 +24,13 @@ constexpr int kRows = 64;   // query rows per workgroup
 constexpr int kKeys = 32;   // keys per K/V tile
 constexpr float kLn2 = 0.69314718055994531f;
 
+// The value of another lane of the same quad, chosen by a DPP quad_perm
+// control (two bits per destination lane: the source lane within the quad).
+template <int kQuadPerm>
+__device__ __forceinline__ float quad_swap(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kQuadPerm, 0xf, 0xf, false));
+}
+
 template <int D>
 __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p) {
   constexpr int kVec = D / 16;  // float4 slices per lane
@@ -117,10 +124,13 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p) {
         part = __builtin_fmaf(qv[u].z, kk.z, part);
         part = __builtin_fmaf(qv[u].w, kk.w, part);
       }
-      // fixed-order quad sum: ((r0 + r1) + (r2 + r3)) on every lane
-      const float a1 = __shfl_xor(part, 1);
+      // fixed-order quad sum: ((r0 + r1) + (r2 + r3)) on every lane; the
+      // partner values come through DPP quad permutations (lanes 1,0,3,2
+      // and 2,3,0,1 of each quad), a vector operation each instead of an
+      // LDS round trip
+      const float a1 = quad_swap<0xB1>(part);
       const float p01 = (r & 1) ? (a1 + part) : (part + a1);
-      const float a2 = __shfl_xor(p01, 2);
+      const float a2 = quad_swap<0x4E>(p01);
       const float sc = (r & 2) ? (a2 + p01) : (p01 + a2);
       const int key = kb + j;
       const bool hidden = key >= N || (causal && key > myq) || (wl >= 0 && key < myq - wl);
