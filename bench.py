@@ -59,6 +59,7 @@ BWD_KERNELS = "bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel"
 # sources each forward kernel is compiled from (its launch, host code aside)
 FWD_SOURCES = ("fa_fwd_mfma.hip", "fa_mfma_common.h", "fa_internal.h")
 FP8_SOURCES = ("fa_fwd_fp8.hip", "fa_mfma_common.h", "fa_internal.h")
+F32_SOURCES = ("fa_fwd_f32.hip", "fa_internal.h")
 
 
 def kernel_source_hash(sources=FWD_SOURCES) -> str:
@@ -447,7 +448,8 @@ def run(args, name, with_cpu):
               "window_left": w.window_left, "scale": w.scale, "seed": w.seed, "flops_per_step": flops}
     rec = make_record(args, t, metric=metric, work=flops, unit="TFLOP/s", peak=peak,
                       bound="mfma" if w.dtype != "f32" else "alu", dtype=w.dtype, config=config,
-                      kernel=KERNEL_NAME[w.dtype], traffic=measured_traffic(name))
+                      kernel=KERNEL_NAME[w.dtype],
+                      traffic=measured_traffic(name, F32_SOURCES if w.dtype == "f32" else FWD_SOURCES))
     copy_note = calibration_copy(args.copy_calibration)
     if copy_note:
         rec["calibration"] = copy_note

@@ -40,6 +40,7 @@ KERNEL_KEY = "fwd_"
 # sources each forward kernel is compiled from (its launch, host code aside)
 FWD_SOURCES = ("fa_fwd_mfma.hip", "fa_mfma_common.h", "fa_internal.h")
 FP8_SOURCES = ("fa_fwd_fp8.hip", "fa_mfma_common.h", "fa_internal.h")
+F32_SOURCES = ("fa_fwd_f32.hip", "fa_internal.h")
 BWD_SOURCES = ("fa_bwd_mfma.hip", "fa_mfma_common.h", "fa_internal.h")
 DECODE_SOURCES = ("fa_decode.hip", "fa_decode.h", "fa_mfma_common.h", "fa_internal.h")
 
@@ -52,6 +53,8 @@ def sources_of(kernel_key: str, fp8: bool = False):
         return BWD_SOURCES
     if "decode" in kernel_key:
         return DECODE_SOURCES
+    if "f32" in kernel_key:
+        return F32_SOURCES
     return FWD_SOURCES
 
 

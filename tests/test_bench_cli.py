@@ -49,6 +49,7 @@ def test_bench_and_profiling_hash_the_same_sources():
     assert profiling.sources_of("bwd_dkdv_kernel") == profiling.BWD_SOURCES
     assert profiling.sources_of("decode_split") == profiling.DECODE_SOURCES
     assert profiling.sources_of("fwd_fp8") == profiling.FP8_SOURCES
+    assert profiling.sources_of("fwd_f32_kernel") == profiling.F32_SOURCES == bench.F32_SOURCES
     assert profiling.sources_of("fwd_") == profiling.FWD_SOURCES
     for srcs in (profiling.FWD_SOURCES, profiling.FP8_SOURCES, profiling.BWD_SOURCES, profiling.DECODE_SOURCES):
         for fn in srcs:
