@@ -160,7 +160,7 @@ def main():
     args = ap.parse_args()
     global KERNEL_KEY
     KERNEL_KEY = args.kernel
-    forward = args.kernel in ("fwd_", "fwd_fp8")
+    forward = args.kernel in ("fwd_", "fwd_fp8", "fwd_f32")
     sources = sources_of(args.kernel, args.fp8)
     name = args.name or f"fwd_{args.workload}"
 
