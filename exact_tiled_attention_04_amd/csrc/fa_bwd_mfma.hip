@@ -694,7 +694,13 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p) {
     }
     barrier_all();
   }
-  if (myq < Nq) store_row<E, D>((unsigned short*)p.dq + q_head + (long long)myq * q_rs, dq, p.scale, hh);
+  // the output row is rebuilt from the lane index (through an empty asm
+  // statement) rather than kept in registers across the key loop
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int myq_out = wq0 + (ln & 31);
+  if (myq_out < Nq)
+    store_row<E, D>((unsigned short*)p.dq + q_head + (long long)myq_out * q_rs, dq, p.scale, ln >> 5);
 }
 
 template <typename E, int D, bool kPacked>
