@@ -83,3 +83,17 @@ def test_calibration_uses_only_the_large_copy(tmp_path, monkeypatch):
     attn, copy = profiling.counter_per_dispatch(str(tmp_path))
     assert copy["FETCH_SIZE"] == [524300.0, 524298.0]
     assert attn["FETCH_SIZE"] == [1000.0]
+
+
+def test_clock_adjusted_fraction():
+    """The line prices the achieved rate against the peak scaled to the clock
+    read during the timed calls (matrix- and ALU-bound kernels only)."""
+    import bench
+    t = {"sclk_mhz": {"mean": 1800.0, "samples": 3}, "warm_s": 1.0}
+    out = bench.clock_fields(t, {"rate_at_avg": 1000.0}, 2400.0, "mfma")
+    assert out["frac_of_peak_at_measured_clock"] == round(1000.0 / (2400.0 * 1800.0 / 2400.0), 4)
+    assert "frac_of_peak_at_measured_clock" not in bench.clock_fields(t, {"rate_at_avg": 5.0}, 8000.0, "hbm")
+    assert "frac_of_peak_at_measured_clock" not in bench.clock_fields(
+        {"sclk_mhz": None, "warm_s": 1.0}, {"rate_at_avg": 1.0}, 1.0, "mfma")
+    assert "frac_of_peak_at_measured_clock" not in bench.clock_fields(
+        {"sclk_mhz": {"error": "no amdsmi"}, "warm_s": 1.0}, {"rate_at_avg": 1.0}, 1.0, "mfma")
