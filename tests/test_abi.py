@@ -223,6 +223,47 @@ def test_fp8_validation_rejects(over, status):
     assert _lib.fa_last_error() != ""
 
 
+# Size limits: fake addresses 16 TiB apart, so that no span overlaps another and
+# only the size rules (32-bit offsets within one head, one launch's grid) can
+# reject the call.
+FAR = 1 << 44
+FAR_FWD = dict(q=1 * FAR, k=2 * FAR, v=3 * FAR, o=4 * FAR, lse=5 * FAR)
+FAR_BWD = dict(FAR_FWD, dout=6 * FAR, dq=7 * FAR, dk=8 * FAR, dv=9 * FAR, work=10 * FAR)
+
+
+@pytest.mark.parametrize("dtype,over,what", [
+    (_lib.FA_DTYPE_BF16, dict(N=2 ** 24, d=64), "too long"),        # 2^24 * 64 * 2 B = 2 GiB per head
+    (_lib.FA_DTYPE_F16, dict(N=2 ** 23, d=128), "too long"),        # 2^23 * 128 * 2 B = 2 GiB
+    (_lib.FA_DTYPE_F32, dict(N=2 ** 22, d=128), "too long"),        # 2^22 * 128 * 4 B = 2 GiB
+    (_lib.FA_DTYPE_BF16, dict(N=2 ** 23 - 2 ** 12, d=128), "too long"),   # within 1 MiB of the limit
+    (_lib.FA_DTYPE_BF16, dict(B=2 ** 20, Hq=2 ** 12, Hkv=2 ** 12, N=1), "launch"),   # 2^32 row blocks
+    (_lib.FA_DTYPE_F32, dict(B=2 ** 19, Hq=2 ** 12, Hkv=2 ** 12, N=1), "launch"),    # 2^31 row blocks
+])
+def test_size_limits_forward(dtype, over, what):
+    assert call(dtype=dtype, **dict(FAR_FWD, **over)) == _lib.FA_ERR_UNSUPPORTED
+    assert what in _lib.fa_last_error()
+
+
+@pytest.mark.parametrize("over", [
+    dict(N=2 ** 24, d=64),
+    dict(N=2 ** 23, d=128),
+    dict(B=2 ** 20, Hq=2 ** 12, Hkv=2 ** 12, N=1),
+])
+def test_size_limits_backward(over):
+    assert call_bwd(**dict(FAR_BWD, **over)) == _lib.FA_ERR_UNSUPPORTED
+    assert _lib.fa_last_error() != ""
+
+
+@pytest.mark.parametrize("over", [
+    dict(N=2 ** 24, d=128),                          # 2^24 * 128 * 1 B = 2 GiB per head
+    dict(N=2 ** 25, d=64),
+    dict(B=2 ** 20, Hq=2 ** 12, Hkv=2 ** 12, N=1),
+])
+def test_size_limits_fp8(over):
+    assert call_fp8(**dict(FAR_FWD, **over)) == _lib.FA_ERR_UNSUPPORTED
+    assert _lib.fa_last_error() != ""
+
+
 def test_fp8_empty_problem_is_a_noop():
     assert call_fp8(B=0, q=0, k=0, v=0, o=0, lse=0) == _lib.FA_OK
     assert call_fp8(N=0) == _lib.FA_OK
