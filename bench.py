@@ -238,15 +238,19 @@ def cpu_baseline_bwd(w, q, k, v, do, budget_s: float = 12.0, gpu=None):
 
 
 class ClockSampler:
-    """Shader-clock readings from the driver's metrics table (amdsmi
-    ``current_gfxclks``, one value per XCD; the firmware refreshes it about
-    once per second), taken every few milliseconds in a background thread.
-    ``window(t0, t1)`` returns the readings taken between two
-    ``time.perf_counter()`` instants.  Empty when amdsmi is unavailable."""
+    """Shader-clock and socket-power readings from the driver's metrics table
+    (amdsmi ``current_gfxclks``, one value per XCD, and
+    ``current_socket_power`` in W; the firmware refreshes them about once per
+    second), taken every few milliseconds in a background thread, plus the
+    board's power cap.  ``window(t0, t1)`` returns the clock readings taken
+    between two ``time.perf_counter()`` instants, ``power_window`` the power
+    readings.  Empty when amdsmi is unavailable."""
 
     def __init__(self, period_s: float = 0.005):
         import threading
         self.samples = []
+        self.power = []
+        self.power_cap_w = None
         self.error = None
         self._stop = threading.Event()
         try:
@@ -257,6 +261,12 @@ class ClockSampler:
         except Exception as e:  # no driver access: report no clock
             self.error = repr(e)
             return
+        try:
+            cap = amdsmi.amdsmi_get_power_cap_info(self._h).get("power_cap")
+            if isinstance(cap, (int, float)) and cap > 0:
+                self.power_cap_w = cap / 1e6  # reported in microwatts
+        except Exception:
+            pass
         self._thread = threading.Thread(target=self._run, args=(period_s,), daemon=True)
         self._thread.start()
 
@@ -267,8 +277,12 @@ class ClockSampler:
                 clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float))]
                 if not clks and isinstance(m.get("current_gfxclk"), (int, float)):
                     clks = [m["current_gfxclk"]]
+                now = time.perf_counter()
                 if clks:
-                    self.samples.append((time.perf_counter(), sum(clks) / len(clks)))
+                    self.samples.append((now, sum(clks) / len(clks)))
+                pw = m.get("current_socket_power")
+                if isinstance(pw, (int, float)) and pw > 0:
+                    self.power.append((now, float(pw)))
             except Exception as e:
                 self.error = repr(e)
                 return
@@ -282,6 +296,9 @@ class ClockSampler:
     def window(self, t0, t1):
         return [c for t, c in self.samples if t0 <= t <= t1]
 
+    def power_window(self, t0, t1):
+        return [w for t, w in self.power if t0 <= t <= t1]
+
 
 def time_steps(step, args, label, stream):
     """W untimed calls, then more untimed calls until at least
@@ -293,7 +310,9 @@ def time_steps(step, args, label, stream):
 
     Returns a dict: ``wall`` (seconds for the K calls), ``per_call_ms``,
     ``warmup_extra`` (calls beyond W), ``warm_s``, and ``sclk_mhz`` (clock
-    readings taken during the timed calls, or the last one before them)."""
+    readings taken during the timed calls, or the last one before them) and
+    ``power_w`` (socket power during the timed calls and the board's cap, or
+    None)."""
     import numpy as np
     import torch
     clock = ClockSampler()
@@ -334,7 +353,13 @@ def time_steps(step, args, label, stream):
                 "source": "amdsmi current_gfxclks, mean over XCDs (refreshed about once per second)"}
     elif clock.error:
         sclk = {"error": clock.error[:200]}
-    return {"wall": t1 - t0, "per_call_ms": per_call, "warmup_extra": extra, "warm_s": warm_s, "sclk_mhz": sclk}
+    watts = clock.power_window(t0, t1)
+    power = None
+    if watts:
+        power = {"mean": round(float(np.mean(watts)), 1), "samples": len(watts), "cap": clock.power_cap_w,
+                 "source": "amdsmi current_socket_power during the timed calls; cap from amdsmi_get_power_cap_info"}
+    return {"wall": t1 - t0, "per_call_ms": per_call, "warmup_extra": extra, "warm_s": warm_s, "sclk_mhz": sclk,
+            "power_w": power}
 
 
 def timing_fields(t, flops_or_bytes, scale=1e12):
@@ -387,6 +412,8 @@ NOMINAL_SCLK_MHZ = 2400.0
 
 def clock_fields(t, tf, peak, bound):
     out = {"sclk_mhz": t["sclk_mhz"], "warm_s": round(t["warm_s"], 3)}
+    if t.get("power_w"):
+        out["power_w"] = t["power_w"]
     s = t["sclk_mhz"]
     mhz = s.get("mean") if isinstance(s, dict) else None
     if bound != "hbm" and mhz:

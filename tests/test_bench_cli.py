@@ -97,3 +97,15 @@ def test_clock_adjusted_fraction():
         {"sclk_mhz": None, "warm_s": 1.0}, {"rate_at_avg": 1.0}, 1.0, "mfma")
     assert "frac_of_peak_at_measured_clock" not in bench.clock_fields(
         {"sclk_mhz": {"error": "no amdsmi"}, "warm_s": 1.0}, {"rate_at_avg": 1.0}, 1.0, "mfma")
+
+
+def test_power_reading_passes_through():
+    """Socket power read during the timed calls (with the board's cap) is
+    carried into the line's clock object when the driver reports it."""
+    import bench
+    pw = {"mean": 1370.0, "samples": 4, "cap": 1400.0, "source": "amdsmi"}
+    t = {"sclk_mhz": {"mean": 1800.0, "samples": 3}, "warm_s": 1.0, "power_w": pw}
+    assert bench.clock_fields(t, {"rate_at_avg": 1.0}, 2400.0, "mfma")["power_w"] == pw
+    t["power_w"] = None
+    assert "power_w" not in bench.clock_fields(t, {"rate_at_avg": 1.0}, 2400.0, "mfma")
+    assert "power_w" not in bench.clock_fields({"sclk_mhz": None, "warm_s": 1.0}, {"rate_at_avg": 1.0}, 1.0, "hbm")
