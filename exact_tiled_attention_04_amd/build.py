@@ -93,5 +93,30 @@ def build(verbose: bool = False, sanitize: bool = False) -> str:
     return lib_path
 
 
+C_CALLER_SRC = os.path.join(ROOT, "tests", "c_caller", "fa_c_caller.c")
+C_CALLER_BIN = os.path.join(ROOT, "tests", "c_caller", "fa_c_caller")
+
+
+def build_c_caller(verbose: bool = False) -> str:
+    """Compile the plain C caller of the library (its GPU test runs it) with
+    gcc as C99, against include/fa.h and the HIP runtime's C API, linked to
+    the in-tree libfa.so (found through an rpath relative to the binary)."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    gcc = shutil.which("gcc") or "gcc"
+    cmd = [gcc, "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-isystem", os.path.join(rocm, "include"), "-I", INCLUDE, C_CALLER_SRC, "-o", C_CALLER_BIN + ".tmp",
+           "-L", PKG, "-lfa", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../exact_tiled_attention_04_amd", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise RuntimeError("C caller build failed:\n" + r.stdout.decode(errors="replace"))
+    os.replace(C_CALLER_BIN + ".tmp", C_CALLER_BIN)
+    return C_CALLER_BIN
+
+
 if __name__ == "__main__":
     build(verbose="-v" in sys.argv, sanitize="--sanitize-host" in sys.argv)
+    if "--sanitize-host" not in sys.argv:
+        build_c_caller(verbose="-v" in sys.argv)
