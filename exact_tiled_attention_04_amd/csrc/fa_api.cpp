@@ -226,10 +226,11 @@ int run_bwd_varlen(const void* q, const void* k, const void* v, const void* o, c
     return fail(FA_ERR_UNSUPPORTED, "max_seqlen_q=%d / max_seqlen_k=%d too long (one sequence's rows must stay "
                 "below 2 GiB)", max_q, max_k);
   const long long rows = fa::bwd_rows_per_workgroup();
+  const long long keys = fa::bwd_keys_per_workgroup(d);
   // the launches round the (sequence, key/value head) groups up to a multiple of 8
   const long long groups8 = 8 * (((long long)B * Hkv + 7) / 8);
   const long long items_q = groups8 * (Hq / Hkv) * ((max_q + rows - 1) / rows);
-  const long long items_k = groups8 * ((max_k + rows - 1) / rows);
+  const long long items_k = groups8 * ((max_k + keys - 1) / keys);
   if (items_q > fa::kMaxGridItems || items_k > fa::kMaxGridItems || (long long)Hq * total_q / 16 > fa::kMaxGridItems)
     return fail(FA_ERR_UNSUPPORTED, "too many sequences, heads or rows for one launch");
   fa::BwdArgs a;
@@ -522,8 +523,10 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   if ((uint64_t)N * d * 2 + (1u << 20) > (uint64_t)INT32_MAX)
     return fail(FA_ERR_UNSUPPORTED, "N=%d too long for d=%d (one head must stay below 2 GiB)", N, d);
   const long long rows = fa::bwd_rows_per_workgroup();
+  const long long keys = fa::bwd_keys_per_workgroup(d);
   const long long items = (long long)B * Hq * ((N + rows - 1) / rows);
-  if (items > fa::kMaxGridItems || (long long)B * Hq * N / 16 > fa::kMaxGridItems)
+  const long long items_k = (long long)B * Hkv * ((N + keys - 1) / keys);
+  if (items > fa::kMaxGridItems || items_k > fa::kMaxGridItems || (long long)B * Hq * N / 16 > fa::kMaxGridItems)
     return fail(FA_ERR_UNSUPPORTED, "B*Hq*N too large for one launch");
   fa::BwdArgs a;
   a.q = q;

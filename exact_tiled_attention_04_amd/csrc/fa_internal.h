@@ -171,7 +171,7 @@ struct BwdParams {
   int causal;
   int window_left;   // -1 = none (normalised: a window reaching key 0 from every row becomes -1)
   int n_blocks;      // ceil(N / 128): query blocks (dQ)
-  int n_kblocks;     // key blocks (dK/dV): ceil(N / 128), packed ceil(max_seqlen_k / 128)
+  int n_kblocks;     // key blocks of the dK/dV launch (its block size: bwd_keys_per_workgroup)
   int items_dq;      // B * Hq * n_blocks
   int items_dkv;     // B * Hkv * n_kblocks
   float scale;
@@ -225,7 +225,8 @@ inline BwdParams make_bwd_params(const BwdArgs& a, int rows_per_wg) {
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_f16(const BwdArgs& a, hipStream_t stream);
-long long bwd_rows_per_workgroup();
+long long bwd_rows_per_workgroup();            // query rows of a dQ workgroup
+long long bwd_keys_per_workgroup(int d);       // keys of a dK/dV workgroup at head dimension d
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t stream);
